@@ -1,0 +1,97 @@
+"""AdaS-Attn (AdaSpark adaptive cube-selective attention) on MI355X.
+
+The computation lives in libadas.so (hand-written HIP for gfx950, C ABI in
+include/adas.h).  This package is its Python binding (``_lib``) plus
+``AdasAttention``, which owns the device buffers of one layer and chains the
+four library calls:
+
+    cube partition (Q, K, V) -> cube mean keys -> Top-p selection -> attention
+
+Torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._lib import (  # noqa: F401
+    ADAS_BF16, ADAS_F32, ADAS_WS_ATTN, ADAS_WS_SELECT, AdasError, Geometry, LIB_PATH,
+    adas_cube_mean_keys, adas_cube_partition, adas_select_topp, adas_sel_capacity,
+    adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
+)
+
+__all__ = [
+    "Geometry", "AdasAttention", "AdasError", "adas_cube_partition", "adas_cube_mean_keys",
+    "adas_select_topp", "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
+    "adas_version", "load", "LIB_PATH",
+]
+
+
+class AdasAttention:
+    """Buffers and call sequence for one AdaS-Attn layer on one device.
+
+    has_video: video query rows are present (prefill); False for decode.
+    n_extra:   text / decode query tokens; n_text_kv: text K/V tokens
+               (0 or n_extra).
+    """
+
+    def __init__(self, geom: Geometry, dtype: torch.dtype, p: float, has_video: bool = True,
+                 n_extra: int = 0, n_text_kv: int = 0, device="cuda"):
+        load()
+        self.geom, self.dtype, self.p = geom, dtype, float(p)
+        self.has_video, self.n_extra, self.n_text_kv = has_video, n_extra, n_text_kv
+        g = geom
+        dev = torch.device(device)
+        e = dict(device=dev, dtype=dtype)
+        self.k_cube = torch.empty((g.n_kv_heads, g.N, g.head_dim), **e)
+        self.v_cube = torch.empty((g.n_kv_heads, g.N, g.head_dim), **e)
+        self.perm = torch.empty((g.N,), device=dev, dtype=torch.int32)
+        self.kbar = torch.empty((g.n_kv_heads, g.n_cubes, g.head_dim), device=dev, dtype=torch.float32)
+        self.q_cube = torch.empty((g.n_q_heads, g.N, g.head_dim), **e) if has_video else None
+        self.out_raster = torch.empty((g.N, g.n_q_heads, g.head_dim), **e) if has_video else None
+        self.out_extra = torch.empty((n_extra, g.n_q_heads, g.head_dim), **e) if n_extra else None
+        rows = (g.N if has_video else 0) + n_extra
+        self.sel_count = torch.empty((g.n_q_heads, rows), device=dev, dtype=torch.int32)
+        cap = adas_sel_capacity(g, has_video, n_extra)
+        if cap < 0:
+            raise AdasError(2, "AdasAttention", "invalid geometry")
+        self.sel_idx = torch.empty((max(cap, 1),), device=dev, dtype=torch.int32)
+        wsb = adas_workspace_bytes(g, dtype, ADAS_WS_ATTN, has_video, n_extra)
+        self.ws = torch.empty((max(wsb, 1),), device=dev, dtype=torch.uint8) if wsb else None
+
+    # -- steps ---------------------------------------------------------------
+    def build_kv(self, k_raster: torch.Tensor, v_raster: torch.Tensor, stream=None):
+        """Partition K and V into cube layout and compute the cube mean keys."""
+        g = self.geom
+        adas_cube_partition(g, k_raster, self.k_cube, self.perm, stream)
+        adas_cube_partition(g, v_raster, self.v_cube, None, stream)
+        adas_cube_mean_keys(g, self.k_cube, self.kbar, stream)
+
+    def partition_queries(self, q_raster: torch.Tensor, stream=None):
+        adas_cube_partition(self.geom, q_raster, self.q_cube, None, stream)
+
+    def select(self, q_extra: Optional[torch.Tensor] = None, p: Optional[float] = None, stream=None):
+        adas_select_topp(self.geom, self.q_cube, q_extra, self.kbar, self.p if p is None else p,
+                         self.sel_count, self.sel_idx, None, stream)
+
+    def attend(self, q_extra=None, k_text=None, v_text=None, stream=None):
+        adas_sparse_attn_fwd(self.geom, self.q_cube, self.k_cube, self.v_cube, q_extra, k_text, v_text,
+                             self.sel_count, self.sel_idx, self.out_raster, self.out_extra, self.ws,
+                             stream)
+
+    def forward(self, q_raster, k_raster, v_raster, q_extra=None, k_text=None, v_text=None,
+                stream=None):
+        """Whole path: partition Q/K/V, mean keys, selection, attention."""
+        self.build_kv(k_raster, v_raster, stream)
+        if self.has_video:
+            self.partition_queries(q_raster, stream)
+        self.select(q_extra, stream=stream)
+        self.attend(q_extra, k_text, v_text, stream)
+        return self.out_raster, self.out_extra
+
+    def decode_step(self, q_extra, stream=None):
+        """Selection plus attention for extra rows over an already built cache."""
+        self.select(q_extra, stream=stream)
+        self.attend(q_extra, None, None, stream)
+        return self.out_extra

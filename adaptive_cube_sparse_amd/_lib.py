@@ -1,0 +1,260 @@
+"""ctypes binding of libadas (include/adas.h).
+
+Argument marshalling only: every function here checks tensor dtypes, devices
+and shapes, turns tensors into raw pointers and calls the C entry point of
+the same name on the current HIP stream.  No step of the computation runs in
+Python.  If the compiled library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libadas.so")
+
+ADAS_OK, ADAS_ERR_NULL, ADAS_ERR_SHAPE, ADAS_ERR_VALUE, ADAS_ERR_DTYPE, \
+    ADAS_ERR_WORKSPACE, ADAS_ERR_CAPACITY, ADAS_ERR_HIP = range(8)
+ADAS_BF16, ADAS_F32 = 0, 1
+ADAS_WS_SELECT, ADAS_WS_ATTN = 0, 1
+ADAS_MAX_HEADS = 128
+ADAS_MAX_CUBES = 4096
+
+EXPORTS = (
+    "adas_cube_partition", "adas_cube_mean_keys", "adas_select_topp",
+    "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
+    "adas_status_string", "adas_last_error", "adas_version",
+)
+
+
+class AdasError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: status {status}: {message}")
+        self.status = status
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "H", "W", "ct", "ch", "cw", "n_q_heads", "n_kv_heads", "head_dim")] + \
+               [("head_map", ctypes.POINTER(ctypes.c_int32))]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libadas.so (built in-tree); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libadas.so not found at {LIB_PATH}; build it with "
+                          f"`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    gp = ctypes.POINTER(_Geom)
+    sig = {
+        "adas_cube_partition": (i32, [gp, i32, i32, vp, vp, vp, vp]),
+        "adas_cube_mean_keys": (i32, [gp, i32, vp, vp, vp]),
+        "adas_select_topp": (i32, [gp, i32, vp, i32, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
+        "adas_sparse_attn_fwd": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, sz, vp]),
+        "adas_workspace_bytes": (sz, [gp, i32, i32, i32, i32]),
+        "adas_sel_capacity": (i64, [gp, i32, i32]),
+        "adas_status_string": (ctypes.c_char_p, [i32]),
+        "adas_last_error": (ctypes.c_char_p, []),
+        "adas_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# geometry
+# ---------------------------------------------------------------------------
+@dataclass
+class Geometry:
+    """Frame grid T x H x W, cube extents (ct, ch, cw) = (t, h, w), heads."""
+    T: int
+    H: int
+    W: int
+    ct: int
+    ch: int
+    cw: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    head_map: Optional[Sequence[int]] = None
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def S(self) -> int:
+        return self.ct * self.ch * self.cw
+
+    @property
+    def n_cubes(self) -> int:
+        return self.N // self.S
+
+    def _c(self):
+        g = _Geom(self.T, self.H, self.W, self.ct, self.ch, self.cw, self.n_q_heads,
+                  self.n_kv_heads, self.head_dim)
+        keep = None
+        if self.head_map is not None:
+            keep = (ctypes.c_int32 * len(self.head_map))(*[int(x) for x in self.head_map])
+            g.head_map = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
+        return g, keep
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ADAS_BF16
+    if t.dtype == torch.float32:
+        return ADAS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _shape(t: Optional[torch.Tensor], shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str):
+    if status != ADAS_OK:
+        lib = load()
+        msg = lib.adas_last_error().decode() or lib.adas_status_string(status).decode()
+        raise AdasError(status, where, msg)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def adas_cube_partition(geom: Geometry, x_raster: torch.Tensor, x_cube: torch.Tensor,
+                        perm: Optional[torch.Tensor] = None, stream=None) -> None:
+    """x_raster [N][nh][d] -> x_cube [nh][N][d] (+ perm [N] int32)."""
+    lib = load()
+    N, nh, d = x_raster.shape
+    _shape(x_cube, (nh, N, d), "x_cube")
+    _shape(perm, (N,), "perm")
+    g, keep = geom._c()
+    st = lib.adas_cube_partition(ctypes.byref(g), _dtype_code(x_raster), nh,
+                                 _ptr(x_raster, name="x_raster"),
+                                 _ptr(x_cube, x_raster.dtype, "x_cube"),
+                                 _ptr(perm, torch.int32, "perm"), _stream(stream))
+    _check(st, "adas_cube_partition")
+
+
+def adas_cube_mean_keys(geom: Geometry, k_cube: torch.Tensor, kbar: torch.Tensor,
+                        stream=None) -> None:
+    """k_cube [Hkv][N][d] -> kbar [Hkv][Nc][d] float32."""
+    lib = load()
+    _shape(k_cube, (geom.n_kv_heads, geom.N, geom.head_dim), "k_cube")
+    _shape(kbar, (geom.n_kv_heads, geom.n_cubes, geom.head_dim), "kbar")
+    g, keep = geom._c()
+    st = lib.adas_cube_mean_keys(ctypes.byref(g), _dtype_code(k_cube), _ptr(k_cube, name="k_cube"),
+                                 _ptr(kbar, torch.float32, "kbar"), _stream(stream))
+    _check(st, "adas_cube_mean_keys")
+
+
+def adas_select_topp(geom: Geometry, q_cube: Optional[torch.Tensor], q_extra: Optional[torch.Tensor],
+                     kbar: torch.Tensor, p: float, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Top-p cube sets for video rows (q_cube [Hq][N][d]) and extra rows
+    (q_extra [n_extra][Hq][d]); see adas.h for the output layout."""
+    lib = load()
+    ref = q_cube if q_cube is not None else q_extra
+    n_extra = 0 if q_extra is None else q_extra.shape[0]
+    _shape(q_cube, (geom.n_q_heads, geom.N, geom.head_dim), "q_cube")
+    if q_extra is not None:
+        _shape(q_extra, (n_extra, geom.n_q_heads, geom.head_dim), "q_extra")
+    rows = (geom.N if q_cube is not None else 0) + n_extra
+    _shape(sel_count, (geom.n_q_heads, rows), "sel_count")
+    g, keep = geom._c()
+    st = lib.adas_select_topp(ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, ref.dtype, "q_cube"),
+                              n_extra, _ptr(q_extra, ref.dtype, "q_extra"),
+                              _ptr(kbar, torch.float32, "kbar"), float(p),
+                              _ptr(sel_count, torch.int32, "sel_count"),
+                              _ptr(sel_idx, torch.int32, "sel_idx"), sel_idx.numel(),
+                              _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream))
+    _check(st, "adas_select_topp")
+
+
+def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text, v_text,
+                         sel_count, sel_idx, out_raster, out_extra,
+                         ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Attention over selected cubes plus own cube (video rows) or selected
+    cubes plus causal text (extra rows); see adas.h."""
+    lib = load()
+    ref = q_cube if q_cube is not None else q_extra
+    n_extra = 0 if q_extra is None else q_extra.shape[0]
+    n_text_kv = 0 if k_text is None else k_text.shape[0]
+    Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
+    _shape(q_cube, (Hq, geom.N, d), "q_cube")
+    _shape(k_cube, (Hkv, geom.N, d), "k_cube")
+    _shape(v_cube, (Hkv, geom.N, d), "v_cube")
+    _shape(out_raster, (geom.N, Hq, d), "out_raster")
+    if n_extra:
+        _shape(q_extra, (n_extra, Hq, d), "q_extra")
+        _shape(out_extra, (n_extra, Hq, d), "out_extra")
+    if n_text_kv:
+        _shape(k_text, (n_text_kv, Hkv, d), "k_text")
+        _shape(v_text, (n_text_kv, Hkv, d), "v_text")
+    dt = ref.dtype
+    g, keep = geom._c()
+    st = lib.adas_sparse_attn_fwd(
+        ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, dt, "q_cube"), _ptr(k_cube, dt, "k_cube"),
+        _ptr(v_cube, dt, "v_cube"), n_extra, n_text_kv, _ptr(q_extra, dt, "q_extra"),
+        _ptr(k_text, dt, "k_text"), _ptr(v_text, dt, "v_text"),
+        _ptr(sel_count, torch.int32, "sel_count"), _ptr(sel_idx, torch.int32, "sel_idx"),
+        _ptr(out_raster, dt, "out_raster"), _ptr(out_extra, dt, "out_extra"),
+        _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "adas_sparse_attn_fwd")
+
+
+def adas_workspace_bytes(geom: Geometry, dtype: torch.dtype, kind: int, has_video: bool,
+                         n_extra: int) -> int:
+    lib = load()
+    g, keep = geom._c()
+    code = ADAS_BF16 if dtype == torch.bfloat16 else ADAS_F32
+    return int(lib.adas_workspace_bytes(ctypes.byref(g), code, kind, int(has_video), n_extra))
+
+
+def adas_sel_capacity(geom: Geometry, has_video: bool, n_extra: int) -> int:
+    lib = load()
+    g, keep = geom._c()
+    return int(lib.adas_sel_capacity(ctypes.byref(g), int(has_video), n_extra))
+
+
+def adas_version() -> str:
+    return load().adas_version().decode()

@@ -1,0 +1,261 @@
+// Host side of the libadas C ABI: argument validation, geometry derivation,
+// workspace sizing and kernel launch selection.  Nothing here touches device
+// memory contents; every check runs before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "adas.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+adas_status fail(adas_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+adas_status ok() {
+  g_last_error[0] = '\0';
+  return ADAS_OK;
+}
+
+// Validate the geometry and derive the kernel view plus head groups.
+adas_status derive(const adas_geom* geom, adas::KGeom& g, adas::HeadGroups& hg) {
+  if (geom == nullptr) return fail(ADAS_ERR_NULL, "geom is NULL");
+  const adas_geom& s = *geom;
+  if (s.T <= 0 || s.H <= 0 || s.W <= 0 || s.ct <= 0 || s.ch <= 0 || s.cw <= 0)
+    return fail(ADAS_ERR_SHAPE, "grid and cube extents must be positive");
+  if (s.T % s.ct || s.H % s.ch || s.W % s.cw)
+    return fail(ADAS_ERR_SHAPE, "cube %dx%dx%d (t,h,w) does not divide grid %dx%dx%d", s.ct, s.ch,
+                s.cw, s.T, s.H, s.W);
+  const long long N = (long long)s.T * s.H * s.W;
+  if (N > (1LL << 30)) return fail(ADAS_ERR_SHAPE, "too many tokens (%lld)", N);
+  if (s.head_dim != 64 && s.head_dim != 128)
+    return fail(ADAS_ERR_SHAPE, "head_dim must be 64 or 128 (got %d)", s.head_dim);
+  if (s.n_q_heads <= 0 || s.n_kv_heads <= 0 || s.n_q_heads > ADAS_MAX_HEADS ||
+      s.n_kv_heads > ADAS_MAX_HEADS)
+    return fail(ADAS_ERR_SHAPE, "head counts must be in [1, %d]", ADAS_MAX_HEADS);
+  g.T = s.T; g.H = s.H; g.W = s.W;
+  g.ct = s.ct; g.ch = s.ch; g.cw = s.cw;
+  g.nT = s.T / s.ct; g.nH = s.H / s.ch; g.nW = s.W / s.cw;
+  g.N = (int)N;
+  g.S = s.ct * s.ch * s.cw;
+  g.Nc = g.nT * g.nH * g.nW;
+  g.Hq = s.n_q_heads;
+  g.Hkv = s.n_kv_heads;
+  g.D = s.head_dim;
+  int map[ADAS_MAX_HEADS];
+  if (s.head_map == nullptr) {
+    if (s.n_q_heads % s.n_kv_heads)
+      return fail(ADAS_ERR_SHAPE, "n_kv_heads (%d) must divide n_q_heads (%d) without head_map",
+                  s.n_kv_heads, s.n_q_heads);
+    const int rep = s.n_q_heads / s.n_kv_heads;
+    for (int h = 0; h < s.n_q_heads; ++h) map[h] = h / rep;
+  } else {
+    for (int h = 0; h < s.n_q_heads; ++h) {
+      map[h] = s.head_map[h];
+      if (map[h] < 0 || map[h] >= s.n_kv_heads)
+        return fail(ADAS_ERR_VALUE, "head_map[%d] = %d out of range [0, %d)", h, map[h],
+                    s.n_kv_heads);
+    }
+  }
+  int k = 0;
+  hg.gmax = 0;
+  for (int gg = 0; gg < s.n_kv_heads; ++gg) {
+    hg.start[gg] = (int16_t)k;
+    for (int h = 0; h < s.n_q_heads; ++h)
+      if (map[h] == gg) hg.heads[k++] = (uint8_t)h;
+    const int sz = k - hg.start[gg];
+    if (sz > hg.gmax) hg.gmax = sz;
+  }
+  hg.start[s.n_kv_heads] = (int16_t)k;
+  return ADAS_OK;
+}
+
+adas_status check_dtype(adas_dtype dt) {
+  if (dt != ADAS_BF16 && dt != ADAS_F32) return fail(ADAS_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  return ADAS_OK;
+}
+
+adas_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ADAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int64_t capv_of(const adas::KGeom& g, bool has_video) {
+  return has_video ? (int64_t)g.S * g.Nc * (g.Nc - 1) / 2 : 0;
+}
+
+int64_t capacity_of(const adas::KGeom& g, bool has_video, int n_extra) {
+  return (int64_t)g.Hq * capv_of(g, has_video) + (int64_t)g.Hq * n_extra * g.Nc;
+}
+
+}  // namespace
+
+extern "C" {
+
+adas_status adas_cube_partition(const adas_geom* geom, adas_dtype dtype, int32_t n_heads,
+                                const void* x_raster, void* x_cube, int32_t* perm,
+                                void* stream) {
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  adas_status st = derive(geom, g, hg);
+  if (st != ADAS_OK) return st;
+  if ((st = check_dtype(dtype)) != ADAS_OK) return st;
+  if (x_raster == nullptr || x_cube == nullptr) return fail(ADAS_ERR_NULL, "x_raster/x_cube is NULL");
+  if (n_heads <= 0 || n_heads > ADAS_MAX_HEADS)
+    return fail(ADAS_ERR_SHAPE, "n_heads must be in [1, %d]", ADAS_MAX_HEADS);
+  const int eb = dtype == ADAS_BF16 ? 2 : 4;
+  return hip_status(adas::launch_partition(g, eb, n_heads, x_raster, x_cube, perm,
+                                           (hipStream_t)stream),
+                    "adas_cube_partition launch");
+}
+
+adas_status adas_cube_mean_keys(const adas_geom* geom, adas_dtype dtype, const void* k_cube,
+                                float* kbar, void* stream) {
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  adas_status st = derive(geom, g, hg);
+  if (st != ADAS_OK) return st;
+  if ((st = check_dtype(dtype)) != ADAS_OK) return st;
+  if (k_cube == nullptr || kbar == nullptr) return fail(ADAS_ERR_NULL, "k_cube/kbar is NULL");
+  return hip_status(adas::launch_mean_keys(g, dtype, k_cube, kbar, (hipStream_t)stream),
+                    "adas_cube_mean_keys launch");
+}
+
+adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                             int32_t n_extra, const void* q_extra, const float* kbar, float p,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
+                             size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;  // the selection keeps its logits in LDS; no workspace
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  adas_status st = derive(geom, g, hg);
+  if (st != ADAS_OK) return st;
+  if ((st = check_dtype(dtype)) != ADAS_OK) return st;
+  if (!(p > 0.0f && p <= 1.0f)) return fail(ADAS_ERR_VALUE, "p must be in (0, 1] (got %g)", (double)p);
+  if (n_extra < 0) return fail(ADAS_ERR_SHAPE, "n_extra must be >= 0");
+  if (q_cube == nullptr && n_extra == 0) return fail(ADAS_ERR_SHAPE, "no query rows");
+  if (n_extra > 0 && q_extra == nullptr) return fail(ADAS_ERR_NULL, "q_extra is NULL");
+  if (kbar == nullptr || sel_count == nullptr || sel_idx == nullptr)
+    return fail(ADAS_ERR_NULL, "kbar/sel_count/sel_idx is NULL");
+  if (g.Nc > ADAS_MAX_CUBES)
+    return fail(ADAS_ERR_SHAPE, "%d cubes exceed the selection limit %d", g.Nc, ADAS_MAX_CUBES);
+  const bool has_video = q_cube != nullptr;
+  const int64_t need = capacity_of(g, has_video, n_extra);
+  if (sel_cap < need)
+    return fail(ADAS_ERR_CAPACITY, "sel_cap %lld < required %lld", (long long)sel_cap,
+                (long long)need);
+  adas::SelectArgs a;
+  a.g = g;
+  a.hg = hg;
+  a.q_cube = q_cube;
+  a.q_extra = q_extra;
+  a.kbar = kbar;
+  a.n_extra = n_extra;
+  a.p = p;
+  a.sel_count = sel_count;
+  a.sel_idx = sel_idx;
+  a.capv = capv_of(g, has_video);
+  a.rows_per_head = (has_video ? g.N : 0) + n_extra;
+  a.has_video = has_video;
+  return hip_status(adas::launch_select(a, dtype, (hipStream_t)stream), "adas_select_topp launch");
+}
+
+static adas_status build_attn(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                              int32_t n_extra, int32_t n_text_kv, adas::AttnArgs& a) {
+  adas_status st = derive(geom, a.g, a.hg);
+  if (st != ADAS_OK) return st;
+  if ((st = check_dtype(dtype)) != ADAS_OK) return st;
+  if (n_extra < 0) return fail(ADAS_ERR_SHAPE, "n_extra must be >= 0");
+  if (n_text_kv != 0 && n_text_kv != n_extra)
+    return fail(ADAS_ERR_SHAPE, "n_text_kv must be 0 or n_extra (%d), got %d", n_extra, n_text_kv);
+  if (q_cube == nullptr && n_extra == 0) return fail(ADAS_ERR_SHAPE, "no query rows");
+  a.has_video = q_cube != nullptr;
+  a.n_extra = n_extra;
+  a.n_text_kv = n_text_kv;
+  a.capv = capv_of(a.g, a.has_video);
+  a.rows_per_head = (a.has_video ? a.g.N : 0) + n_extra;
+  adas::plan_attention(a, dtype);
+  return ADAS_OK;
+}
+
+adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                 const void* k_cube, const void* v_cube, int32_t n_extra,
+                                 int32_t n_text_kv, const void* q_extra, const void* k_text,
+                                 const void* v_text, const int32_t* sel_count,
+                                 const int32_t* sel_idx, void* out_raster, void* out_extra,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  adas::AttnArgs a;
+  adas_status st = build_attn(geom, dtype, q_cube, n_extra, n_text_kv, a);
+  if (st != ADAS_OK) return st;
+  if (k_cube == nullptr || v_cube == nullptr || sel_count == nullptr || sel_idx == nullptr)
+    return fail(ADAS_ERR_NULL, "k_cube/v_cube/sel_count/sel_idx is NULL");
+  if (q_cube != nullptr && out_raster == nullptr) return fail(ADAS_ERR_NULL, "out_raster is NULL");
+  if (n_extra > 0 && (q_extra == nullptr || out_extra == nullptr))
+    return fail(ADAS_ERR_NULL, "q_extra/out_extra is NULL");
+  if (n_text_kv > 0 && (k_text == nullptr || v_text == nullptr))
+    return fail(ADAS_ERR_NULL, "k_text/v_text is NULL");
+  const size_t need = adas::attention_workspace_bytes(a, dtype);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  a.q_cube = q_cube;
+  a.k_cube = k_cube;
+  a.v_cube = v_cube;
+  a.q_extra = q_extra;
+  a.k_text = k_text;
+  a.v_text = v_text;
+  a.sel_count = sel_count;
+  a.sel_idx = sel_idx;
+  a.out_raster = out_raster;
+  a.out_extra = out_extra;
+  a.partials = (float*)ws;
+  return hip_status(adas::launch_attention(a, dtype, (hipStream_t)stream),
+                    "adas_sparse_attn_fwd launch");
+}
+
+size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kind kind,
+                            int32_t has_video, int32_t n_extra) {
+  if (kind == ADAS_WS_SELECT) return 0;  // logits stay in LDS
+  adas::AttnArgs a;
+  const int dummy = 1;
+  if (build_attn(geom, dtype, has_video ? &dummy : nullptr, n_extra, 0, a) != ADAS_OK) return 0;
+  return adas::attention_workspace_bytes(a, dtype);
+}
+
+int64_t adas_sel_capacity(const adas_geom* geom, int32_t has_video, int32_t n_extra) {
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  if (derive(geom, g, hg) != ADAS_OK || n_extra < 0) return -1;
+  return capacity_of(g, has_video != 0, n_extra);
+}
+
+const char* adas_status_string(adas_status s) {
+  switch (s) {
+    case ADAS_OK: return "ADAS_OK";
+    case ADAS_ERR_NULL: return "ADAS_ERR_NULL: a required pointer is NULL";
+    case ADAS_ERR_SHAPE: return "ADAS_ERR_SHAPE: inconsistent shape arguments";
+    case ADAS_ERR_VALUE: return "ADAS_ERR_VALUE: argument value out of range";
+    case ADAS_ERR_DTYPE: return "ADAS_ERR_DTYPE: unknown dtype";
+    case ADAS_ERR_WORKSPACE: return "ADAS_ERR_WORKSPACE: workspace too small";
+    case ADAS_ERR_CAPACITY: return "ADAS_ERR_CAPACITY: selection buffer too small";
+    case ADAS_ERR_HIP: return "ADAS_ERR_HIP: HIP runtime error";
+  }
+  return "unknown adas_status";
+}
+
+const char* adas_last_error(void) { return g_last_error; }
+
+const char* adas_version(void) { return "0.1"; }
+
+}  // extern "C"

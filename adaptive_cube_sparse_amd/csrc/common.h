@@ -1,0 +1,246 @@
+// Shared device helpers and launch descriptors for the AdaS-Attn kernels
+// (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "adas.h"
+
+namespace adas {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Geometry as the kernels see it (all derived on the host).
+struct KGeom {
+  int T, H, W;
+  int ct, ch, cw;
+  int nT, nH, nW;
+  int N;     // tokens
+  int S;     // tokens per cube
+  int Nc;    // cubes
+  int Hq, Hkv, D;
+};
+
+// Query heads grouped by the KV head they read.  Heads of group g are
+// heads[start[g] .. start[g+1]).
+struct HeadGroups {
+  int16_t start[ADAS_MAX_HEADS + 1];
+  uint8_t heads[ADAS_MAX_HEADS];
+  int gmax;  // largest group
+};
+
+// ---------------------------------------------------------------------------
+// cube geometry
+// ---------------------------------------------------------------------------
+// Raster token index of cube-layout position (c, r).
+__device__ __forceinline__ int raster_of(const KGeom& g, int c, int r) {
+  const int bx = c % g.nW;
+  const int t1 = c / g.nW;
+  const int by = t1 % g.nH;
+  const int bt = t1 / g.nH;
+  const int dx = r % g.cw;
+  const int t2 = r / g.cw;
+  const int dy = t2 % g.ch;
+  const int dt = t2 / g.ch;
+  const int f = bt * g.ct + dt, y = by * g.ch + dy, x = bx * g.cw + dx;
+  return (f * g.H + y) * g.W + x;
+}
+
+// Offset of a video row's list in sel_idx (closed form, see adas.h).
+__device__ __forceinline__ int64_t video_list_offset(int64_t capv, int hq, int S, int c, int r) {
+  return (int64_t)hq * capv + (int64_t)S * c * (c - 1) / 2 + (int64_t)r * c;
+}
+__device__ __forceinline__ int64_t extra_list_offset(int64_t capv, int Hq, int n_extra, int Nc, int hq,
+                                                     int m) {
+  return (int64_t)Hq * capv + ((int64_t)hq * n_extra + m) * Nc;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+// round to nearest even (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ __bf16 f32_to_bf16(float f) {
+  return __builtin_bit_cast(__bf16, f32_to_bf16_bits(f));
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions.  The xor butterfly gives bit-identical results on every
+// lane (each step adds the same two operands on both partners), so decisions
+// taken on the result are wave-uniform.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
+// number of set bits of m in lanes below this one
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+__device__ __forceinline__ float fast_exp(float x) {
+  // exp(x) = 2^(x*log2 e); v_exp_f32 is accurate to ~1 ulp on normal results.
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// ---------------------------------------------------------------------------
+// Top-p on one row held by one wave (key design 2, the S_i equation).
+//
+// E[i] (lane L) is exp(z_j - max z) for candidate j = L + 64*i, or -1 for
+// j >= n (padding).  Z is the wave-uniform sum of the valid E.  Finds the
+// Top-p set under the order (E descending, j ascending) and writes its ids
+// ascending to out[0..count).  Returns count (wave-uniform).
+//
+// Method: the selected set is {E > tau} plus the lowest-index ties at tau,
+// where tau is the largest float with mass(E >= tau) >= p*Z.  tau is found
+// by bisection on the float bit pattern (positive floats order like their
+// bits), stopping as soon as one element is left between the bounds.
+// ---------------------------------------------------------------------------
+template <int NPL>
+__device__ int topp_select_row(float (&E)[NPL], int n, float Z, float p, int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (n <= 0) return 0;
+  if (p >= 1.0f) {
+    for (int j = lane; j < n; j += kWave) out[j] = j;
+    return n;
+  }
+  const float target = p * Z;
+  uint32_t lo = 0u, hi = 0x3F800001u;  // mass(E >= lo) >= target > mass(E >= hi)
+  int cnt_lo = n, cnt_hi = 0;
+  float tau;
+  for (;;) {
+    if (cnt_lo - cnt_hi == 1) {
+      // exactly one element in [lo, hi): it is the cut element
+      float best = -1.0f;
+      const float fhi = __uint_as_float(hi);
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (E[i] >= __uint_as_float(lo) && E[i] < fhi) best = fmaxf(best, E[i]);
+      tau = wave_max(best);
+      break;
+    }
+    if (hi - lo <= 1u) {
+      tau = __uint_as_float(lo);
+      break;
+    }
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    const float fm = __uint_as_float(mid);
+    float ms = 0.0f;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const bool ge = E[i] >= fm;
+      ms += ge ? E[i] : 0.0f;
+      cnt += popc64(__ballot(ge));
+    }
+    ms = wave_sum(ms);
+    if (ms >= target) {
+      lo = mid;
+      cnt_lo = cnt;
+    } else {
+      hi = mid;
+      cnt_hi = cnt;
+    }
+  }
+  // mass strictly above tau and the number of ties at tau
+  float mgt = 0.0f;
+  int ceq = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    mgt += E[i] > tau ? E[i] : 0.0f;
+    ceq += popc64(__ballot(E[i] == tau));
+  }
+  mgt = wave_sum(mgt);
+  int keq = ceq;
+  if (tau > 0.0f) {
+    const float need = (target - mgt) / tau;
+    int k = (int)ceilf(need);
+    if (k < 1) k = 1;
+    if (k < keq) keq = k;
+  }
+  // ascending compaction: stripe i holds candidates 64*i .. 64*i+63
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool eq = E[i] == tau;
+    const uint64_t beq = __ballot(eq);
+    const int eq_rank = eq_seen + lanes_below(beq);
+    const bool sel = (E[i] > tau) || (eq && eq_rank < keq);
+    const uint64_t bs = __ballot(sel);
+    if (sel) out[base + lanes_below(bs)] = lane + kWave * i;
+    base += popc64(bs);
+    eq_seen += popc64(beq);
+  }
+  return base;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch entry points (defined in the .hip files)
+// ---------------------------------------------------------------------------
+hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, const void* src, void* dst,
+                            int32_t* perm, hipStream_t s);
+hipError_t launch_mean_keys(const KGeom& g, adas_dtype dt, const void* k, float* kbar,
+                            hipStream_t s);
+
+struct SelectArgs {
+  KGeom g;
+  HeadGroups hg;
+  const void* q_cube;   // may be null
+  const void* q_extra;  // may be null
+  const float* kbar;
+  int n_extra;
+  float p;
+  int32_t* sel_count;
+  int32_t* sel_idx;
+  int64_t capv;  // per-head video capacity (0 without video rows)
+  int rows_per_head;  // Nv + n_extra
+  int has_video;
+};
+hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s);
+
+struct AttnArgs {
+  KGeom g;
+  HeadGroups hg;
+  const void* q_cube;
+  const void* k_cube;
+  const void* v_cube;
+  const void* q_extra;
+  const void* k_text;
+  const void* v_text;
+  const int32_t* sel_count;
+  const int32_t* sel_idx;
+  void* out_raster;
+  void* out_extra;
+  float* partials;  // workspace for split extra rows
+  int n_extra;
+  int n_text_kv;
+  int64_t capv;
+  int rows_per_head;
+  int has_video;
+  // schedule (filled by plan_attention)
+  int extra_tiles_per_group;
+  int extra_chunks;
+  int extra_chunk_cubes;
+};
+void plan_attention(AttnArgs& a, adas_dtype dt);
+size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt);
+hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s);
+
+}  // namespace adas

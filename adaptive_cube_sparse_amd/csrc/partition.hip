@@ -1,0 +1,123 @@
+// Cube partition (AdaSpark, papernotes.org, key design 1: h x w x t cubes as
+// the atomic unit) and cube mean keys (key design 2: kbar_j).
+//
+// Both kernels are HBM-bound streaming passes.
+//   partition : reads and writes every element once (2 * bytes of the tensor)
+//   mean keys : reads K once, writes Nc*d floats
+#include "common.h"
+
+namespace adas {
+
+// One workgroup copies one cube of one head: S rows of `vpr` 16-byte vectors.
+// Rows are contiguous on both sides, so every 16-byte access is part of a
+// fully used row segment; the destination is written sequentially.
+__global__ __launch_bounds__(256) void k_partition(const uint4* __restrict__ src,
+                                                   uint4* __restrict__ dst,
+                                                   int32_t* __restrict__ perm, KGeom g, int nh,
+                                                   int vpr) {
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  // cube -> block coordinates (uniform per workgroup)
+  const int bx = c % g.nW;
+  const int by = (c / g.nW) % g.nH;
+  const int bt = c / (g.nW * g.nH);
+  const int hw = g.ch * g.cw;
+  const size_t dst_row0 = ((size_t)h * g.N + (size_t)c * g.S);
+  const int total = g.S * vpr;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int r = e / vpr;
+    const int v = e - r * vpr;
+    const int dt = r / hw;
+    const int rem = r - dt * hw;
+    const int dy = rem / g.cw;
+    const int dx = rem - dy * g.cw;
+    const int n = ((bt * g.ct + dt) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
+    dst[(dst_row0 + r) * vpr + v] = src[((size_t)n * nh + h) * vpr + v];
+    if (perm != nullptr && h == 0 && v == 0) perm[c * g.S + r] = n;
+  }
+}
+
+hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, const void* src, void* dst,
+                            int32_t* perm, hipStream_t s) {
+  const int vpr = g.D * elem_bytes / 16;
+  dim3 grid(g.Nc, nh);
+  hipLaunchKernelGGL(k_partition, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, g,
+                     nh, vpr);
+  return hipGetLastError();
+}
+
+// One wave per (kv head, cube).  Lanes are laid out LPR per row (16 bytes
+// each) and RPI = 64 / LPR rows per step; each lane accumulates its EPV
+// columns in float64, then the RPI row groups are folded with xor shuffles.
+// Every cube size S is a power of two in the configurations this serves, so
+// the float64 sum of bf16 values is exact and the final division by S is
+// exact; the single float32 rounding then matches any exact evaluation.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_mean_keys(const T* __restrict__ k, float* __restrict__ kbar,
+                                                   KGeom g) {
+  constexpr int EPV = 16 / sizeof(T);     // elements per 16-byte vector
+  constexpr int LPR = D / EPV;            // lanes per row
+  constexpr int RPI = kWave / LPR;        // rows per step
+  const int lane = threadIdx.x & (kWave - 1);
+  const int cube = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (cube >= g.Hkv * g.Nc) return;
+  const int col = (lane % LPR) * EPV;
+  const int r0 = lane / LPR;
+  const T* base = k + (size_t)cube * g.S * D;  // (kv, j) cube rows are contiguous
+  double acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+  for (int r = r0; r < g.S; r += RPI) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + (size_t)r * D + col);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+        acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    } else {
+      acc[0] += (double)__uint_as_float(raw.x);
+      acc[1] += (double)__uint_as_float(raw.y);
+      acc[2] += (double)__uint_as_float(raw.z);
+      acc[3] += (double)__uint_as_float(raw.w);
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  if (lane < LPR) {
+    float res[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) res[e] = (float)(acc[e] / (double)g.S);
+    float* dst = kbar + (size_t)cube * D + col;
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(res[e], res[e + 1], res[e + 2], res[e + 3]);
+  }
+}
+
+hipError_t launch_mean_keys(const KGeom& g, adas_dtype dt, const void* k, float* kbar,
+                            hipStream_t s) {
+  const int cubes = g.Hkv * g.Nc;
+  dim3 grid((cubes + 3) / 4);
+  if (dt == ADAS_BF16) {
+    if (g.D == 128)
+      hipLaunchKernelGGL((k_mean_keys<uint16_t, 128>), grid, dim3(256), 0, s, (const uint16_t*)k,
+                         kbar, g);
+    else
+      hipLaunchKernelGGL((k_mean_keys<uint16_t, 64>), grid, dim3(256), 0, s, (const uint16_t*)k,
+                         kbar, g);
+  } else {
+    if (g.D == 128)
+      hipLaunchKernelGGL((k_mean_keys<float, 128>), grid, dim3(256), 0, s, (const float*)k, kbar,
+                         g);
+    else
+      hipLaunchKernelGGL((k_mean_keys<float, 64>), grid, dim3(256), 0, s, (const float*)k, kbar,
+                         g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace adas

@@ -1,0 +1,195 @@
+/*
+ * adas.h -- C ABI of libadas, AdaS-Attn (adaptive cube-selective attention)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (AdaSpark, CVPR 2026; papernotes.org summary, "关键设计" items
+ * 1, 2 and 4; thelatestinai.com listing, Figure 2 caption):
+ *   1. video tokens on a T x H x W grid are cut into h x w x t cubes;
+ *   2. every cube j gets a mean key kbar_j;
+ *   3. a query in cube i scores the preceding cubes,
+ *      P_i = softmax_j(q . kbar_j / sqrt(d_k)), j < i;
+ *   4. it keeps the Top-p set S_i: the fewest cubes, highest P first (equal P:
+ *      lower cube index first), whose probabilities sum to at least p;
+ *   5. it attends, with one exact softmax, to the tokens of S_i plus all
+ *      tokens of its own cube.
+ * Text queries select among all video cubes and attend causally to the text
+ * tokens up to themselves; decode queries select among all cubes of a video
+ * KV cache and attend to the selected cubes only.
+ *
+ * Conventions shared by every call
+ * ---------------------------------
+ *  * Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    allocates no device memory; scratch memory is the caller's workspace
+ *    (ws, ws_bytes), sized by adas_workspace_bytes().
+ *  * Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream).  Arguments are validated on the host
+ *    before anything is launched; on an error nothing is launched and the
+ *    outputs are untouched.  A launch failure returns ADAS_ERR_HIP.  A
+ *    thread-local message describing the last error is kept for
+ *    adas_last_error().
+ *  * Shapes: N = T*H*W tokens, S = ct*ch*cw tokens per cube, Nc = N / S cubes.
+ *    Cube c of raster token n = (f*H + y)*W + x is
+ *    c = ((f/ct)*(H/ch) + y/ch)*(W/cw) + x/cw, its offset inside the cube is
+ *    r = ((f%ct)*ch + y%ch)*cw + x%cw, and its cube-layout position is c*S + r.
+ *  * dtype ADAS_BF16: bfloat16 Q/K/V/outputs, MFMA kernels, head_dim 64 or
+ *    128, S a multiple of 16.  ADAS_F32: float32 throughout (reference-grade
+ *    kernels for small problems), head_dim 64 or 128.
+ *  * Grouped-query attention: query head hq reads KV head head_map[hq]
+ *    (head_map NULL: hq / (Hq/Hkv), which needs Hkv | Hq).
+ *  * The library keeps no state between calls and is re-entrant.
+ */
+#ifndef ADAS_H
+#define ADAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADAS_VERSION_MAJOR 0
+#define ADAS_VERSION_MINOR 1
+
+#define ADAS_MAX_HEADS 128   /* limit on n_q_heads and n_kv_heads            */
+#define ADAS_MAX_CUBES 4096  /* limit on Nc for selection (candidates/row)   */
+
+typedef enum {
+  ADAS_OK = 0,
+  ADAS_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  ADAS_ERR_SHAPE = 2,      /* grid/cube/head/size arguments are inconsistent  */
+  ADAS_ERR_VALUE = 3,      /* p outside (0, 1], head_map entry out of range   */
+  ADAS_ERR_DTYPE = 4,      /* unknown dtype                                   */
+  ADAS_ERR_WORKSPACE = 5,  /* ws_bytes smaller than adas_workspace_bytes()    */
+  ADAS_ERR_CAPACITY = 6,   /* sel_cap smaller than adas_sel_capacity()        */
+  ADAS_ERR_HIP = 7         /* a HIP launch or runtime call failed             */
+} adas_status;
+
+typedef enum { ADAS_BF16 = 0, ADAS_F32 = 1 } adas_dtype;
+
+/* Problem geometry.  Passed by pointer; read on the host only. */
+typedef struct {
+  int32_t T, H, W;          /* frame grid in tokens: frames, rows, columns    */
+  int32_t ct, ch, cw;       /* cube extents t, h, w; each divides T, H, W     */
+  int32_t n_q_heads;        /* Hq                                             */
+  int32_t n_kv_heads;       /* Hkv                                            */
+  int32_t head_dim;         /* d_k (64 or 128)                                */
+  const int32_t* head_map;  /* HOST array [Hq] -> kv head, or NULL            */
+} adas_geom;
+
+/* Which call a workspace is sized for. */
+typedef enum { ADAS_WS_SELECT = 0, ADAS_WS_ATTN = 1 } adas_ws_kind;
+
+/*
+ * adas_cube_partition -- cube partition (papernotes.org, key design 1).
+ * Copies a token-major tensor into the cube-contiguous, head-major layout
+ * used by every other call.  Bit-exact copy.
+ *   x_raster [N][n_heads][d]  input, raster token order (as a QKV projection
+ *                             emits it)
+ *   x_cube   [n_heads][N][d]  output; x_cube[h][c*S + r] = x_raster[n][h]
+ *   perm     [N] int32        optional output (may be NULL): perm[c*S+r] = n
+ * Call once for Q (n_heads = Hq) and once each for K and V (n_heads = Hkv).
+ * Errors: NULL (x_raster/x_cube), SHAPE, DTYPE, HIP.
+ */
+adas_status adas_cube_partition(const adas_geom* geom, adas_dtype dtype, int32_t n_heads,
+                                const void* x_raster, void* x_cube, int32_t* perm,
+                                void* stream);
+
+/*
+ * adas_cube_mean_keys -- cube mean keys kbar_j (papernotes.org, key design 2).
+ *   k_cube [Hkv][N][d]   keys in cube layout
+ *   kbar   [Hkv][Nc][d]  float32 output: (1/S) * sum of cube j's S keys,
+ *                        accumulated in float64, rounded once to float32
+ *                        (round to nearest even).
+ * Errors: NULL, SHAPE, DTYPE, HIP.
+ */
+adas_status adas_cube_mean_keys(const adas_geom* geom, adas_dtype dtype, const void* k_cube,
+                                float* kbar, void* stream);
+
+/*
+ * adas_select_topp -- selection softmax and Top-p cube sets (papernotes.org,
+ * key design 2, the P_i and S_i equations; key design 4, one threshold p).
+ *
+ * Rows: video rows (hq, pos) for pos in [0, N) when q_cube != NULL, then
+ * extra rows (hq, m) for m in [0, n_extra) (text or decode queries).
+ * Video row candidates are cubes 0..c-1 of its own cube c; extra rows'
+ * candidates are all Nc cubes.
+ *   q_cube   [Hq][N][d]       video queries in cube layout, or NULL
+ *   n_extra  number of extra query tokens (0 allowed)
+ *   q_extra  [n_extra][Hq][d] extra queries, token-major (NULL iff n_extra==0)
+ *   kbar     [Hkv][Nc][d]     float32 mean keys
+ *   p        threshold in (0, 1]; p == 1 keeps every candidate
+ *   sel_count [Hq][R] int32   output, R = (q_cube ? N : 0) + n_extra:
+ *                             video row pos at [hq*R + pos], extra row m at
+ *                             [hq*R + Nv + m] (Nv = N or 0)
+ *   sel_idx  int32 [sel_cap]  output: each row's selected cube ids, ascending,
+ *                             at a closed-form offset:
+ *                               CapV = S*Nc*(Nc-1)/2 (0 without video rows)
+ *                               video (hq, pos), c = pos/S, r = pos%S:
+ *                                 hq*CapV + S*c*(c-1)/2 + r*c
+ *                               extra (hq, m): Hq*CapV + (hq*n_extra + m)*Nc
+ *                             Entries past a row's count are not written.
+ *   sel_cap  capacity of sel_idx in entries (>= adas_sel_capacity()).
+ *   ws, ws_bytes  workspace (adas_workspace_bytes(ADAS_WS_SELECT, ...)).
+ * Ordering: cubes are ranked by (P descending, cube index ascending); the
+ * scores are computed to float32 accuracy from the float32 kbar.
+ * Errors: NULL, SHAPE (Nc > ADAS_MAX_CUBES, no rows), VALUE (p, head_map),
+ *         DTYPE, CAPACITY, WORKSPACE, HIP.
+ */
+adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                             int32_t n_extra, const void* q_extra, const float* kbar, float p,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * adas_sparse_attn_fwd -- attention over the selected cubes plus the own cube
+ * (papernotes.org, key design 2: always keep full attention to the own cube).
+ *
+ * One exact softmax (scale 1/sqrt(d)) per row over
+ *   video row (hq, pos):  tokens of its selected cubes and all S tokens of
+ *                         its own cube;
+ *   extra row (hq, m):    tokens of its selected cubes, plus text tokens
+ *                         0..m when n_text_kv > 0 (causal text).
+ *   q_cube, k_cube, v_cube  [Hq|Hkv][N][d] cube layout (q_cube NULL: no video
+ *                           rows, e.g. decode)
+ *   n_extra, q_extra        as in adas_select_topp
+ *   n_text_kv               0 (decode: no text keys) or n_extra (text prefill)
+ *   k_text, v_text          [n_extra][Hkv][d] when n_text_kv > 0, else NULL
+ *   sel_count, sel_idx      the selection (layout as adas_select_topp)
+ *   out_raster [N][Hq][d]   video outputs in raster token order (NULL iff
+ *                           q_cube is NULL)
+ *   out_extra  [n_extra][Hq][d]  extra-row outputs (NULL iff n_extra == 0)
+ *   ws, ws_bytes            workspace (adas_workspace_bytes(ADAS_WS_ATTN, ...))
+ * Selected ids must be ascending, < the row's candidate count, and counts
+ * must not exceed it; the host does not read device lists (undefined
+ * behaviour otherwise).  Outputs are float32-accumulated, stored in dtype.
+ * Errors: NULL, SHAPE, VALUE, DTYPE, WORKSPACE, HIP.
+ */
+adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                 const void* k_cube, const void* v_cube, int32_t n_extra,
+                                 int32_t n_text_kv, const void* q_extra, const void* k_text,
+                                 const void* v_text, const int32_t* sel_count,
+                                 const int32_t* sel_idx, void* out_raster, void* out_extra,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace `kind` needs (host only, no device work).  has_video is
+ * 1 when q_cube will be non-NULL.  Returns 0 for invalid geometry. */
+size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kind kind,
+                            int32_t has_video, int32_t n_extra);
+
+/* Entries sel_idx must hold (host only).  Returns -1 for invalid geometry. */
+int64_t adas_sel_capacity(const adas_geom* geom, int32_t has_video, int32_t n_extra);
+
+/* Static description of a status code. */
+const char* adas_status_string(adas_status s);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* adas_last_error(void);
+
+/* "major.minor" */
+const char* adas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ADAS_H */

@@ -1,0 +1,105 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases run every row and span several row tiles with ragged tails;
+full-size configurations are checked on seeded stratified row samples.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import adas_oracle as O
+from tests.gpu_harness import (Reference, all_rows, check_layout, check_rows, log, run_device,
+                               sampled_rows, bits)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def _case(wl, p=None, head_map=None, rows="all", **kw):
+    log(f"case {wl.name}: grid {wl.T}x{wl.H}x{wl.W} cube t{wl.ct}h{wl.ch}w{wl.cw} "
+        f"heads {wl.n_q_heads}/{wl.n_kv_heads} d {wl.head_dim} {wl.dtype} p {p or wl.p} "
+        f"extra {wl.n_text + wl.n_decode} head_map {head_map}")
+    data = workloads.generate(wl)
+    layer = run_device(wl, data, p=p, head_map=head_map)
+    ref = Reference(wl, data, head_map)
+    check_layout(ref, layer)
+    rws = all_rows(ref) if rows == "all" else sampled_rows(ref, **kw)
+    check_rows(ref, layer, rws, wl.p if p is None else p)
+    return ref, layer
+
+
+# --- small cases: every row ------------------------------------------------------
+SMALL = workloads.Workload(name="small", T=8, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=6,
+                           n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7, seed=31)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_b"])
+def test_tiny_f32(name):
+    _case(workloads.get(name))
+
+
+@pytest.mark.parametrize("p", [0.05, 0.7, 0.95])
+def test_small_bf16(p):
+    # 3 heads per KV group x 64 tokens = 192 rows per query cube: tiles of 128 + 64
+    _case(SMALL, p=p)
+
+
+def test_small_bf16_p1_is_dense_block_causal():
+    ref, layer = _case(SMALL, p=1.0)
+    dense = O.dense_block_causal(ref.data["q"], ref.data["k"], ref.data["v"], ref.g)
+    got = O.to_f64(bits(layer.out_raster))
+    err = np.abs(got - dense)
+    log(f"  p=1 vs dense block-causal: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_small_bf16_head_map_d64():
+    wl = SMALL.replace(name="small_d64", head_dim=64, n_q_heads=5, seed=32)
+    _case(wl, head_map=[1, 0, 1, 1, 0])
+
+
+def test_text_rows_causal_s128():
+    # cube 8x8x2 = 128 tokens (two key blocks per cube) + 70 causal text tokens
+    wl = workloads.Workload(name="text", T=8, H=16, W=16, ct=2, ch=8, cw=8, n_q_heads=4,
+                            n_kv_heads=1, head_dim=128, dtype="bf16", p=0.9, seed=33,
+                            n_text=70, text_kv=True)
+    _case(wl)
+
+
+def test_decode_rows_split():
+    # extra rows only: the attention splits cubes into chunks and merges them
+    wl = workloads.Workload(name="decode_small", T=64, H=16, W=16, ct=4, ch=4, cw=4,
+                            n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7,
+                            seed=34, video_queries=False, n_decode=5)
+    _case(wl)
+
+
+def test_many_cubes_small_cube():
+    # Nc = 1152 > 1024 candidates (wide selection path), S = 16 (partial key blocks)
+    wl = workloads.Workload(name="many_cubes", T=72, H=16, W=16, ct=1, ch=4, cw=4,
+                            n_q_heads=2, n_kv_heads=1, head_dim=128, dtype="bf16", p=0.5,
+                            seed=35)
+    _case(wl, rows="sample", cubes_per_decile=3, tokens_per_cube=8)
+
+
+def test_deterministic():
+    data = workloads.generate(SMALL)
+    a = run_device(SMALL, data)
+    b = run_device(SMALL, data)
+    assert torch.equal(a.sel_count, b.sel_count)
+    assert torch.equal(a.out_raster.view(torch.int16), b.out_raster.view(torch.int16))
+
+
+# --- full-size configurations: sampled rows ------------------------------------------
+@pytest.mark.parametrize("name", ["qwen3b", "qwen7b_p05", "qwen7b_p07", "qwen7b_p09", "hour", "decode"])
+def test_full_config_sampled(name):
+    _case(workloads.get(name), rows="sample", tokens_per_cube=2, extra_tokens=8)
+
+
+def test_decode_single_step():
+    """One decode step (1 query token x 28 heads) over the full decode cache."""
+    wl = workloads.get("decode").replace(n_decode=1, name="decode_step")
+    _case(wl)
