@@ -19,6 +19,8 @@
 // V^T 18 KB, masks/lists ~2 KB.
 //
 // f32 path: one wave per row on the vector ALUs (small problems).
+#include <cstdlib>
+
 #include "common.h"
 
 namespace adas {
@@ -572,10 +574,17 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_video_ro
 // host side
 // ---------------------------------------------------------------------------
 namespace {
-int attn_tr(const AttnArgs& a) {
-  // small extra-only problems (a decode step) use narrow tiles
-  if (!a.has_video && a.hg.gmax * a.n_extra <= 32) return 32;
-  return 128;
+int attn_tr(const AttnArgs&) { return 128; }
+
+// The union-tile kernel (attn_union.hip) is the default bf16 path; the
+// gathered-row kernel in this file is kept for comparison and selected with
+// ADAS_ATTN_KERNEL=gather.
+bool use_gather_kernel() {
+  static const int v = [] {
+    const char* e = getenv("ADAS_ATTN_KERNEL");
+    return (e != nullptr && e[0] == 'g') ? 1 : 0;
+  }();
+  return v != 0;
 }
 }  // namespace
 
@@ -629,9 +638,26 @@ static hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s) {
   if (dt == ADAS_BF16) {
-    const int TR = attn_tr(a);
-    if (a.g.D == 128) return TR == 128 ? launch_bf16<128, 128>(a, s) : launch_bf16<128, 32>(a, s);
-    return TR == 128 ? launch_bf16<64, 128>(a, s) : launch_bf16<64, 32>(a, s);
+    if (use_gather_kernel())
+      return a.g.D == 128 ? launch_bf16<128, 128>(a, s) : launch_bf16<64, 128>(a, s);
+    hipError_t e = a.g.D == 128 ? launch_union<128>(a, s) : launch_union<64>(a, s);
+    if (e != hipSuccess) return e;
+    if (a.n_extra > 0 && a.extra_chunks > 1) {
+      AttnSched sc;
+      sc.video_tiles_per_group = 0;
+      sc.extra_tiles_per_group = a.extra_tiles_per_group;
+      sc.extra_chunks = a.extra_chunks;
+      sc.extra_chunk_cubes = a.extra_chunk_cubes;
+      sc.n_extra_wgs = a.g.Hkv * sc.extra_tiles_per_group * sc.extra_chunks;
+      const int n_tiles = a.g.Hkv * sc.extra_tiles_per_group;
+      const int waves = n_tiles * 128;
+      if (a.g.D == 128)
+        hipLaunchKernelGGL((k_merge_bf16<128, 128>), dim3((waves + 3) / 4), dim3(256), 0, s, a, sc, n_tiles);
+      else
+        hipLaunchKernelGGL((k_merge_bf16<64, 128>), dim3((waves + 3) / 4), dim3(256), 0, s, a, sc, n_tiles);
+      e = hipGetLastError();
+    }
+    return e;
   }
   const int video_rows = a.has_video ? a.g.Hq * a.g.N : 0;
   const int total = video_rows + a.g.Hq * a.n_extra;

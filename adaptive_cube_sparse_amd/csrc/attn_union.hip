@@ -1,0 +1,458 @@
+// Attention over the selected cubes plus the own cube (AdaSpark,
+// papernotes.org, key design 2) -- bf16 MFMA kernel, union tiles.
+//
+// A workgroup (4 waves) owns a tile of 128 rows that read the same KV head
+// (video rows of one query cube, or extra rows).  Each wave owns 32 rows; its
+// query block and its output accumulators stay in registers for the whole
+// tile.  The workgroup walks the union of its rows' selected cubes (plus the
+// own cube, or the causal text keys), one key block of 64 keys at a time:
+//   * K and V of the block are staged in LDS (V transposed), the next block is
+//     fetched into registers meanwhile;
+//   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, masks
+//     keys of cubes its row did not select (a bit per row and cube, built from
+//     the selection lists), runs the online softmax in float32 and
+//     accumulates O^T += V^T P^T; a wave none of whose rows selected the cube
+//     skips the block.
+// Rows therefore spend MFMA work on every key block of the tile union; the
+// masked part is the price of keeping accumulators in registers.
+//
+// Tile order: extra rows first (heaviest), then video tiles by descending
+// query cube.  When 8 is a multiple of the KV head count, workgroup b runs on
+// XCD b % 8 (round-robin dispatch) and video tiles are dealt so that each XCD
+// serves one KV head, letting concurrently resident tiles share K/V in L2.
+#include "common.h"
+
+namespace adas {
+
+typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+constexpr int UKB = 64;      // keys per key block
+constexpr int UTR = 128;     // rows per tile
+constexpr int UPASS = 1024;  // cubes per selection-bitmap pass
+constexpr float kLog2eU = 1.4426950408889634f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+}  // namespace
+
+struct USched {
+  int video_tiles_per_group;
+  int extra_tiles_per_group;
+  int extra_chunks;
+  int extra_chunk_cubes;
+  int n_extra_wgs;
+  int xcd_mode;  // 1: XCD-aware dealing of video tiles
+};
+
+template <int D>
+struct USmem {
+  static constexpr int KS = D + 8;    // bf16 stride of a K row
+  static constexpr int VS = UKB + 8;  // bf16 stride of a V^T row
+  uint16_t k[UKB * KS];
+  uint16_t vt[D * VS];
+  uint32_t bits[UPASS * 4];  // [cube in pass][wave] -> rows of the wave that selected it
+  uint16_t ulist[UPASS];     // cubes of the pass selected by any row
+  int n_union;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
+  using Sm = USmem<D>;
+  __shared__ Sm sm;
+  const KGeom& g = a.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;  // row of this lane inside the wave
+  const int lh = lane >> 5;  // lane half
+
+  // ---- decode the tile ----------------------------------------------------------
+  bool video;
+  int grp, rho0, c = 0, chunk = 0, tile_e = 0;
+  int b = blockIdx.x;
+  if (b < sc.n_extra_wgs) {
+    video = false;
+    tile_e = b / sc.extra_chunks;
+    chunk = b - tile_e * sc.extra_chunks;
+    grp = tile_e / sc.extra_tiles_per_group;
+    rho0 = (tile_e - grp * sc.extra_tiles_per_group) * UTR;
+  } else {
+    video = true;
+    b -= sc.n_extra_wgs;
+    const int tpg = sc.video_tiles_per_group;
+    if (sc.xcd_mode) {
+      const int x = b & 7, i = b >> 3;
+      const int stride_c = 8 / g.Hkv;
+      grp = x % g.Hkv;
+      const int cpar = x / g.Hkv;
+      const int ci = i / tpg;
+      rho0 = (i - ci * tpg) * UTR;
+      c = g.Nc - 1 - cpar - ci * stride_c;
+      if (c < 0) return;
+    } else {
+      const int per_c = g.Hkv * tpg;
+      c = g.Nc - 1 - b / per_c;
+      const int rem = b % per_c;
+      grp = rem / tpg;
+      rho0 = (rem - grp * tpg) * UTR;
+    }
+  }
+  const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
+  const int group_rows = video ? gsz * g.S : gsz * a.n_extra;
+  const int n_rows = min(UTR, group_rows - rho0);
+  if (n_rows <= 0) return;
+  const int hstart = a.hg.start[grp];
+
+  // ---- this lane's row ------------------------------------------------------------
+  const int t_row = wave * 32 + lr;
+  const bool row_ok = t_row < n_rows;
+  int hq = 0, pos = 0;
+  if (row_ok) {
+    const int rho = rho0 + t_row;
+    if (video) {
+      const int slot = rho / g.S;
+      hq = a.hg.heads[hstart + slot];
+      pos = c * g.S + (rho - slot * g.S);
+    } else {
+      const int slot = rho / a.n_extra;
+      hq = a.hg.heads[hstart + slot];
+      pos = rho - slot * a.n_extra;
+    }
+  }
+  const bool wave_has_rows = wave * 32 < n_rows;
+
+  // Q^T operand: row lr, d = 16*ds + 8*lh + [0..8)
+  bf16x8u qb[D / 16];
+  {
+    const uint16_t* src = video ? (const uint16_t*)a.q_cube + ((size_t)hq * g.N + pos) * D
+                                : (const uint16_t*)a.q_extra + ((size_t)pos * g.Hq + hq) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(src + 16 * ds + 8 * lh);
+      qb[ds] = __builtin_bit_cast(bf16x8u, v);
+    }
+  }
+  const float qscale = kLog2eU / sqrtf((float)D);
+
+  // running softmax state of the lane's row (identical in both lane halves)
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  // ---- K/V staging: 4 x 16 B of K and V per thread (D = 128) --------------------------
+  constexpr int VPR = D / 8;                    // 16-byte vectors per row
+  constexpr int NV = UKB * VPR / 256;           // vectors per thread (4 or 2)
+  uint4 kr[NV], vr[NV];
+  // K: vector e = tid + 256*u -> key e / VPR, chunk e % VPR (row-major copy).
+  // V: thread owns keys 4*kq .. 4*kq+3 of d-chunk vc, transposed on store.
+  auto fetch = [&](const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + 256 * u;
+      const int key = e / VPR, ch = e % VPR;
+      kr[u] = key < kc ? *reinterpret_cast<const uint4*>(kb + key * stride + ch * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+    // V: NV keys (4 for D=128, 2 for D=64) per thread
+    constexpr int KQ = UKB / 4;  // 16 key quads
+    const int kq = tid % KQ, vc = tid / KQ;  // vc < 256/16 = 16 d-chunks
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int key = (NV == 4 ? 4 * kq + u : 4 * kq + 2 * (vc / VPR) + u);
+      const int chv = vc % VPR;
+      vr[u] = key < kc ? *reinterpret_cast<const uint4*>(vb + key * stride + chv * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = tid + 256 * u;
+      const int key = e / VPR, ch = e % VPR;
+      *reinterpret_cast<uint4*>(&sm.k[key * Sm::KS + ch * 8]) = kr[u];
+    }
+    constexpr int KQ = UKB / 4;
+    const int kq = tid % KQ, vc = tid / KQ;
+    const int chv = vc % VPR;
+    const int key0 = NV == 4 ? 4 * kq : 4 * kq + 2 * (vc / VPR);
+    // transpose: element (key0+u, 8*chv+e) -> vt[8*chv+e][key0+u]
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(vr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t h[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const uint32_t word = w[u * 4 + e / 2];
+        h[u] = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+      }
+      uint16_t* dst = &sm.vt[(8 * chv + e) * Sm::VS + key0];
+      if constexpr (NV == 4) {
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      }
+    }
+  };
+
+  // ---- one key block: rowsel = this lane's row takes part --------------------------
+  // kc valid keys; causal: key kbase_idx + key must be <= the row's token index.
+  auto compute = [&](bool rowsel, int kc, bool causal, int kbase_idx) {
+    f32x16 st[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[h2][i] = 0.f;
+      if (32 * h2 < kc) {
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+          const bf16x8u ka = __builtin_bit_cast(
+              bf16x8u, *reinterpret_cast<const uint4*>(&sm.k[(32 * h2 + lr) * Sm::KS + 16 * ds + 8 * lh]));
+          st[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ds], st[h2], 0, 0, 0);
+        }
+      }
+    }
+    // keys of st[h2][i]: 32*h2 + 8*(i/4) + 4*lh + (i%4)
+    float mb = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * h2 + 8 * (i / 4) + 4 * lh + (i % 4);
+        const bool ok = rowsel && key < kc && (!causal || kbase_idx + key <= pos);
+        const float s = ok ? st[h2][i] * qscale : -INFINITY;
+        st[h2][i] = s;
+        mb = fmaxf(mb, s);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float m_new = fmaxf(m_run, mb);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = ex2(m_run - m_use);
+    float ls = 0.f;
+    bf16x8u pb[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const __bf16 p = f32_to_bf16(ex2(st[h2][i] - m_use));
+        ls += (float)p;
+        pb[2 * h2 + i / 8][i % 8] = p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    // O^T += V^T P^T over 4 k-steps of 16 keys; slot 8*lh + e of k-step u
+    // holds key 16*u + 8*(e/4) + 4*lh + (e%4).
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (16 * u < kc) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const uint16_t* vrow = &sm.vt[(32 * db + lr) * Sm::VS + 16 * u + 4 * lh];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+          const bf16x8u va = __builtin_bit_cast(bf16x8u, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], acc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  const int nkb_cube = (g.S + UKB - 1) / UKB;
+  const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.N * D;
+  const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.N * D;
+
+  // ---- own cube (video): every row ------------------------------------------------------
+  if (video) {
+    for (int kb = 0; kb < nkb_cube; ++kb) {
+      const int kc = min(UKB, g.S - kb * UKB);
+      const size_t off = ((size_t)c * g.S + kb * UKB) * D;
+      fetch(kg + off, vg + off, D, kc);
+      __syncthreads();
+      stage();
+      __syncthreads();
+      if (wave_has_rows) compute(row_ok, kc, false, 0);
+    }
+  }
+  // ---- causal text keys (extra rows of a text prefill), chunk 0 --------------------------
+  if (!video && a.n_text_kv > 0 && chunk == 0) {
+    const uint16_t* kt = (const uint16_t*)a.k_text + (size_t)grp * D;
+    const uint16_t* vt = (const uint16_t*)a.v_text + (size_t)grp * D;
+    const int ntb = (a.n_text_kv + UKB - 1) / UKB;
+    for (int tb = 0; tb < ntb; ++tb) {
+      const int kc = min(UKB, a.n_text_kv - tb * UKB);
+      fetch(kt + (size_t)tb * UKB * g.Hkv * D, vt + (size_t)tb * UKB * g.Hkv * D,
+            (size_t)g.Hkv * D, kc);
+      __syncthreads();
+      stage();
+      __syncthreads();
+      const bool any = __ballot(row_ok && pos >= tb * UKB) != 0;
+      if (any) compute(row_ok && pos >= tb * UKB, kc, true, tb * UKB);
+    }
+  }
+
+  // ---- selected cubes -----------------------------------------------------------------
+  // two threads per row walk the row's ascending list
+  const int my_row = tid >> 1, my_half = tid & 1;
+  const int32_t* my_list = nullptr;
+  int my_cnt = 0;
+  if (my_row < n_rows) {
+    const int rho = rho0 + my_row;
+    int64_t off;
+    int hq2, row_index;
+    if (video) {
+      const int slot = rho / g.S;
+      hq2 = a.hg.heads[hstart + slot];
+      const int r = rho - slot * g.S;
+      off = video_list_offset(a.capv, hq2, g.S, c, r);
+      row_index = c * g.S + r;
+    } else {
+      const int slot = rho / a.n_extra;
+      hq2 = a.hg.heads[hstart + slot];
+      const int m = rho - slot * a.n_extra;
+      off = extra_list_offset(a.capv, g.Hq, a.n_extra, g.Nc, hq2, m);
+      row_index = (a.has_video ? g.N : 0) + m;
+    }
+    my_list = a.sel_idx + off;
+    my_cnt = a.sel_count[(size_t)hq2 * a.rows_per_head + row_index];
+  }
+  int cube_lo, cube_hi;
+  if (video) {
+    cube_lo = 0;
+    cube_hi = c;
+  } else {
+    cube_lo = chunk * sc.extra_chunk_cubes;
+    cube_hi = min(g.Nc, cube_lo + sc.extra_chunk_cubes);
+  }
+  for (int jb = cube_lo; jb < cube_hi; jb += UPASS) {
+    const int je = min(cube_hi, jb + UPASS);
+    const int span = je - jb;
+    __syncthreads();  // previous users of bits/ulist/LDS are done
+    for (int e = tid; e < span * 4; e += 256) sm.bits[e] = 0u;
+    __syncthreads();
+    if (my_row < n_rows) {
+      // entries in [jb, je): binary search for both ends (lists ascending)
+      int lo = 0, hi = my_cnt;
+      while (lo < hi) { const int mid = (lo + hi) >> 1; if (my_list[mid] < jb) lo = mid + 1; else hi = mid; }
+      int lo2 = lo, hi2 = my_cnt;
+      while (lo2 < hi2) { const int mid = (lo2 + hi2) >> 1; if (my_list[mid] < je) lo2 = mid + 1; else hi2 = mid; }
+      const uint32_t bit = 1u << (my_row & 31);
+      uint32_t* wbase = &sm.bits[my_row >> 5];
+#pragma unroll 4
+      for (int i = lo + my_half; i < lo2; i += 2) atomicOr(wbase + 4 * (my_list[i] - jb), bit);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int u0 = 0; u0 < span; u0 += 64) {
+        const int u = u0 + lane;
+        bool any = false;
+        if (u < span) any = (sm.bits[4 * u] | sm.bits[4 * u + 1] | sm.bits[4 * u + 2] | sm.bits[4 * u + 3]) != 0u;
+        const uint64_t bal = __ballot(any);
+        if (any) sm.ulist[base + lanes_below(bal)] = (uint16_t)u;
+        base += popc64(bal);
+      }
+      if (lane == 0) sm.n_union = base;
+    }
+    __syncthreads();
+    const int nblocks = sm.n_union * nkb_cube;
+    if (nblocks == 0) continue;
+    {
+      const int j = jb + sm.ulist[0];
+      fetch(kg + (size_t)j * g.S * D, vg + (size_t)j * g.S * D, D, min(UKB, g.S));
+    }
+    for (int it = 0; it < nblocks; ++it) {
+      const int ci = it / nkb_cube, kb = it - ci * nkb_cube;
+      const int ul = sm.ulist[ci];
+      const int kc = min(UKB, g.S - kb * UKB);
+      __syncthreads();  // LDS K/V free
+      stage();
+      __syncthreads();
+      if (it + 1 < nblocks) {
+        const int ci2 = (it + 1) / nkb_cube, kb2 = (it + 1) - ci2 * nkb_cube;
+        const int j2 = jb + sm.ulist[ci2];
+        const size_t off2 = ((size_t)j2 * g.S + kb2 * UKB) * D;
+        fetch(kg + off2, vg + off2, D, min(UKB, g.S - kb2 * UKB));
+      }
+      const uint32_t mw = sm.bits[4 * ul + wave];
+      if (mw != 0u) compute(((mw >> lr) & 1u) != 0u, kc, false, 0);
+    }
+  }
+
+  // ---- epilogue ----------------------------------------------------------------------
+  if (!row_ok) return;
+  // acc[db][i] = O^T[d = 32*db + 8*(i/4) + 4*lh + (i%4)][row]
+  if (!video && sc.extra_chunks > 1) {
+    float* dst = a.partials + ((size_t)tile_e * sc.extra_chunks + chunk) * UTR * (D + 2) +
+                 (size_t)t_row * (D + 2);
+    if (lh == 0) {
+      dst[0] = m_run;
+      dst[1] = l_run;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float* p = dst + 2 + 32 * db + 8 * q + 4 * lh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = acc[db][4 * q + e];
+      }
+    return;
+  }
+  const float inv = 1.0f / l_run;
+  uint16_t* dst;
+  if (video) {
+    const int n = raster_of(g, c, pos - c * g.S);
+    dst = (uint16_t*)a.out_raster + ((size_t)n * g.Hq + hq) * D;
+  } else {
+    dst = (uint16_t*)a.out_extra + ((size_t)pos * g.Hq + hq) * D;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[db][4 * q] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(acc[db][4 * q + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[db][4 * q + 2] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(acc[db][4 * q + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * q + 4 * lh) = make_uint2(w0, w1);
+    }
+}
+
+template <int D>
+hipError_t launch_union(const AttnArgs& a, hipStream_t s) {
+  USched sc;
+  sc.video_tiles_per_group = a.has_video ? (a.hg.gmax * a.g.S + UTR - 1) / UTR : 0;
+  sc.extra_tiles_per_group = a.extra_tiles_per_group;
+  sc.extra_chunks = a.extra_chunks;
+  sc.extra_chunk_cubes = a.extra_chunk_cubes;
+  sc.n_extra_wgs = a.g.Hkv * sc.extra_tiles_per_group * sc.extra_chunks;
+  sc.xcd_mode = (8 % a.g.Hkv) == 0 ? 1 : 0;
+  long video_blocks = 0;
+  if (a.has_video) {
+    if (sc.xcd_mode) {
+      const int stride_c = 8 / a.g.Hkv;
+      video_blocks = 8L * ((a.g.Nc + stride_c - 1) / stride_c) * sc.video_tiles_per_group;
+    } else {
+      video_blocks = (long)a.g.Nc * a.g.Hkv * sc.video_tiles_per_group;
+    }
+  }
+  const long blocks = sc.n_extra_wgs + video_blocks;
+  if (blocks > 0)
+    hipLaunchKernelGGL((k_attn_union<D>), dim3((unsigned)blocks), dim3(256), 0, s, a, sc);
+  return hipGetLastError();
+}
+
+template hipError_t launch_union<128>(const AttnArgs&, hipStream_t);
+template hipError_t launch_union<64>(const AttnArgs&, hipStream_t);
+
+}  // namespace adas

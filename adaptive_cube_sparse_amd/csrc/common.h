@@ -242,5 +242,7 @@ struct AttnArgs {
 void plan_attention(AttnArgs& a, adas_dtype dt);
 size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt);
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s);
+template <int D>
+hipError_t launch_union(const AttnArgs& a, hipStream_t s);
 
 }  // namespace adas

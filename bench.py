@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of the AdaS-Attn hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM: cube partition of Q, K and V, cube mean keys,
+Top-p selection and sparse attention (for the decode workload: selection and
+attention of one decode step over a cache built before timing).
+
+The printed JSON line reports:
+  value       effective TFLOP/s = 4 * d * (attended (row, key) pairs) / step
+              time, counting only the tokens each row attends (selected
+              cubes, own cube, causal text);
+  roofline    the attention kernel alone: algorithmic FLOPs (or bytes for
+              decode) per launch / its mean launch time, timed with HIP events
+              on the launch stream inside the timed region, against the
+              MI355X peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "AdaS-Attn effective TFLOP/s (selected tokens) and % of MI355X bf16/HBM peak"
+DEFAULT_WORKLOAD = "qwen3b"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD,
+                    help="workload name (tiny, qwen3b, qwen7b_p05/p07/p09, hour, decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--decode-batch", type=int, default=1,
+                    help="decode tokens per step for the decode workload (1 = one step)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    path = os.path.join(ROOT, "adaptive_cube_sparse_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_entry(workload: str):
+    """HBM traffic of the attention kernel measured with rocprofv3 counters,
+    if the committed measurement is for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except Exception:
+        return None
+    if not rec or rec.get("attn_hip_sha256_16") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def attended_pairs(layer, wl) -> int:
+    """Sum over rows of the number of keys each row attends."""
+    import torch
+    S = wl.cube_size
+    cnt = layer.sel_count.to(torch.int64)
+    total = 0
+    nv = wl.n_tokens if wl.video_queries else 0
+    if nv:
+        total += int(cnt[:, :nv].sum().item()) * S + nv * wl.n_q_heads * S
+    n_extra = wl.n_text + wl.n_decode
+    if n_extra:
+        total += int(cnt[:, nv:].sum().item()) * S
+        if wl.text_kv:
+            total += wl.n_q_heads * n_extra * (n_extra + 1) // 2
+    return total
+
+
+def decode_unique_bytes(layer, wl) -> int:
+    """Algorithmic HBM bytes of one decode attention launch: K and V of every
+    cube selected by at least one row of a KV head (read once), plus queries,
+    outputs and the selection lists."""
+    import torch
+    g = layer.geom
+    d = g.head_dim
+    cnt = layer.sel_count.cpu().numpy()
+    idx_all = layer.sel_idx
+    Hq, Nc, S = g.n_q_heads, g.n_cubes, g.S
+    rep = Hq // g.n_kv_heads
+    n_extra = wl.n_decode
+    kv_bytes = 0
+    list_entries = 0
+    for kv in range(g.n_kv_heads):
+        used = torch.zeros(Nc, dtype=torch.bool, device=idx_all.device)
+        for hq in range(kv * rep, (kv + 1) * rep):
+            for m in range(n_extra):
+                off = (hq * n_extra + m) * Nc
+                c = int(cnt[hq, m])
+                used[idx_all[off: off + c].long()] = True
+                list_entries += c
+        kv_bytes += int(used.sum().item()) * S * d * 2 * 2
+    qo = 2 * n_extra * Hq * d * 2
+    return kv_bytes + qo + list_entries * 4 + Hq * n_extra * 4
+
+
+def cpu_baseline(wl, data, budget_s: float):
+    """Time the CPU oracle on a bounded, seeded sample of the workload's rows:
+    selection softmax + Top-p + attention per row (partition and mean keys of
+    the whole input are timed too).  BLAS is pinned to one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import adas_oracle as O
+    rng = np.random.default_rng(123)
+    g = O.Geometry.of(wl)
+    flops = 0.0
+    rows = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k_cube, _ = O.partition(data["k"], g)
+        v_cube, _ = O.partition(data["v"], g)
+        q_cube = O.partition(data["q"], g)[0] if wl.video_queries else None
+        kbar = O.mean_keys(k_cube, g)
+        t_layout = time.perf_counter() - t0
+        t_rows = 0.0
+        rep = wl.n_q_heads // wl.n_kv_heads
+        while t_rows < budget_s:
+            hq = int(rng.integers(wl.n_q_heads))
+            t1 = time.perf_counter()
+            if wl.video_queries:
+                pos = int(rng.integers(g.N))
+                c = pos // g.S
+                P = O.selection_probabilities(O.to_f64(q_cube[hq, pos]), kbar[hq // rep][:c])
+                S_ = O.top_p(P, wl.p)
+                O.attention_video_row(q_cube, k_cube, v_cube, g, hq, pos, S_)
+                keys = (len(S_) + 1) * g.S
+            else:
+                m = int(rng.integers(wl.n_decode or wl.n_text))
+                P = O.selection_probabilities(O.to_f64(data["q_text"][m, hq]), kbar[hq // rep])
+                S_ = O.top_p(P, wl.p)
+                O.attention_extra_row(data["q_text"], k_cube, v_cube, g, hq, m, S_)
+                keys = len(S_) * g.S
+            t_rows += time.perf_counter() - t1
+            flops += 4.0 * wl.head_dim * keys
+            rows += 1
+    value = flops / t_rows / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} random rows of {wl.name} (selection softmax, Top-p and attention "
+                      f"per row, float64 NumPy, 1 BLAS thread) in {t_rows:.1f} s; whole-input "
+                      f"partition + mean keys took {t_layout:.1f} s and are not in the rate",
+            "host_threads_available": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    from adaptive_cube_sparse_amd import AdasAttention, Geometry
+
+    wl = workloads.get(args.config)
+    decode = not wl.video_queries
+    if decode:
+        wl = wl.replace(n_decode=args.decode_batch)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    data = workloads.generate(wl)
+    t_gen = time.perf_counter() - t_gen
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    geom = Geometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw, wl.n_q_heads, wl.n_kv_heads, wl.head_dim)
+    n_extra = wl.n_text + wl.n_decode
+    n_text_kv = wl.n_text if wl.text_kv else 0
+    layer = AdasAttention(geom, dt, wl.p, has_video=wl.video_queries, n_extra=n_extra,
+                          n_text_kv=n_text_kv, device=dev)
+    q = up(data["q"]) if wl.video_queries else None
+    k, v = up(data["k"]), up(data["v"])
+    qe = up(data["q_text"]) if n_extra else None
+    kt = up(data["k_text"]) if n_text_kv else None
+    vt = up(data["v_text"]) if n_text_kv else None
+    stream = torch.cuda.current_stream()
+    if decode:
+        layer.build_kv(k, v)   # the cache exists before decoding starts
+
+    ev = {name: [] for name in ("layout", "select", "attention")}
+
+    def step(record):
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+        e0 = mark() if record else None
+        if not decode:
+            layer.build_kv(k, v)
+            layer.partition_queries(q)
+        e1 = mark() if record else None
+        layer.select(qe)
+        e2 = mark() if record else None
+        layer.attend(qe, kt, vt)
+        e3 = mark() if record else None
+        if record:
+            ev["layout"].append((e0, e1))  # partition Q/K/V + mean keys
+            ev["select"].append((e1, e2))
+            ev["attention"].append((e2, e3))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    def mean_ms(pairs):
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
+
+    k_ms = {name: mean_ms(p) for name, p in ev.items() if p}
+    pairs = attended_pairs(layer, wl)
+    flops_step = 4.0 * wl.head_dim * pairs
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    rows = wl.n_q_heads * ((wl.n_tokens if wl.video_queries else 0) + n_extra)
+    attn_ms = k_ms["attention"]
+    if decode:
+        alg_bytes = decode_unique_bytes(layer, wl)
+        achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_entry(wl.name),
+                "algorithmic_bytes_per_launch": alg_bytes}
+    else:
+        achieved = flops_step / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_entry(wl.name),
+                "algorithmic_flops_per_launch": flops_step}
+    roof["kernel"] = "k_attn_bf16" if wl.dtype == "bf16" else "k_attn_f32"
+    roof["launch_ms"] = attn_ms
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, data, args.cpu_seconds)
+
+    dens = None
+    if wl.video_queries:
+        cnt = layer.sel_count[:, : wl.n_tokens].to(torch.float64)
+        cubes = torch.arange(wl.n_tokens, device=dev) // wl.cube_size
+        cand = cubes.to(torch.float64).clamp_min(1)
+        dens = float((cnt / cand)[:, wl.cube_size:].mean().item())
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "grid": [wl.T, wl.H, wl.W],
+                   "cube_thw": [wl.ct, wl.ch, wl.cw], "heads": [wl.n_q_heads, wl.n_kv_heads],
+                   "head_dim": wl.head_dim, "p": wl.p, "extra_queries": n_extra,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_ms": k_ms,
+        "queries_per_s": rows / (ms_step * 1e-3),
+        "attended_pairs": pairs,
+        "mean_selected_fraction": dens,
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
