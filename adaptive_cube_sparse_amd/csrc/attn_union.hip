@@ -20,6 +20,8 @@
 // query cube.  When 8 is a multiple of the KV head count, workgroup b runs on
 // XCD b % 8 (round-robin dispatch) and video tiles are dealt so that each XCD
 // serves one KV head, letting concurrently resident tiles share K/V in L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace adas {
@@ -48,7 +50,7 @@ struct USched {
 template <int D>
 struct USmem {
   static constexpr int KS = D + 8;    // bf16 stride of a K row
-  static constexpr int VS = UKB + 8;  // bf16 stride of a V^T row
+  static constexpr int VS = UKB + 4;  // bf16 stride of a V^T row (34 dwords: conflict-free b64 reads)
   uint16_t k[UKB * KS];
   uint16_t vt[D * VS];
   uint32_t bits[UPASS * 4];  // [cube in pass][wave] -> rows of the wave that selected it
@@ -150,6 +152,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
   uint4 kr[NV], vr[NV];
   // K: vector e = tid + 256*u -> key e / VPR, chunk e % VPR (row-major copy).
   // V: thread owns keys 4*kq .. 4*kq+3 of d-chunk vc, transposed on store.
+  // d-chunk handled by V-staging thread group q: bits 0 and 1 swapped, so the
+  // two 16-lane groups of a 32-lane half write V^T rows 2 chunks apart.
+  auto vchunk_of = [](int q) { return (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1); };
   auto fetch = [&](const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
     }
     // V: NV keys (4 for D=128, 2 for D=64) per thread
     constexpr int KQ = UKB / 4;  // 16 key quads
-    const int kq = tid % KQ, vc = tid / KQ;  // vc < 256/16 = 16 d-chunks
+    const int kq = tid % KQ, vc = vchunk_of(tid / KQ);  // vc < 256/16 = 16 d-chunks
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int key = (NV == 4 ? 4 * kq + u : 4 * kq + 2 * (vc / VPR) + u);
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       *reinterpret_cast<uint4*>(&sm.k[key * Sm::KS + ch * 8]) = kr[u];
     }
     constexpr int KQ = UKB / 4;
-    const int kq = tid % KQ, vc = tid / KQ;
+    const int kq = tid % KQ, vc = vchunk_of(tid / KQ);
     const int chv = vc % VPR;
     const int key0 = NV == 4 ? 4 * kq : 4 * kq + 2 * (vc / VPR);
     // transpose: element (key0+u, 8*chv+e) -> vt[8*chv+e][key0+u]
@@ -202,13 +207,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
 
   // ---- one key block: rowsel = this lane's row takes part --------------------------
   // kc valid keys; causal: key kbase_idx + key must be <= the row's token index.
-  auto compute = [&](bool rowsel, int kc, bool causal, int kbase_idx) {
+  // Scores stay in log2 units (qscale folds 1/sqrt(d) and log2 e).  The running
+  // reference m_run is raised only when a block's max exceeds it by more than
+  // kLazy (P <= 2^kLazy meanwhile), so the accumulators are rescaled rarely.
+  // A lane whose row did not select the block gets bias +inf, i.e. P = 0.
+  constexpr float kLazy = 8.0f;
+  auto compute = [&](auto per_key_mask, bool rowsel, int kc, bool causal, int kbase_idx) {
+    constexpr bool PKM = decltype(per_key_mask)::value;
     f32x16 st[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[h2][i] = 0.f;
-      if (32 * h2 < kc) {
+      if (!PKM || 32 * h2 < kc) {
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
           const bf16x8u ka = __builtin_bit_cast(
@@ -218,43 +229,51 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       }
     }
     // keys of st[h2][i]: 32*h2 + 8*(i/4) + 4*lh + (i%4)
-    float mb = -INFINITY;
+    if constexpr (PKM) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 32 * h2 + 8 * (i / 4) + 4 * lh + (i % 4);
-        const bool ok = rowsel && key < kc && (!causal || kbase_idx + key <= pos);
-        const float s = ok ? st[h2][i] * qscale : -INFINITY;
-        st[h2][i] = s;
-        mb = fmaxf(mb, s);
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * h2 + 8 * (i / 4) + 4 * lh + (i % 4);
+          const bool ok = key < kc && (!causal || kbase_idx + key <= pos);
+          st[h2][i] = ok ? st[h2][i] : -INFINITY;
+        }
+    }
+    float mb = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mb = fmaxf(mb, fmaxf(st[0][i], st[1][i]));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = ex2(m_run - m_use);
+    const float mb_c = rowsel ? mb * qscale : -INFINITY;
+    const bool grow = mb_c > m_run + kLazy;
+    if (__ballot(grow) != 0ull) {
+      // only growing lanes rescale (a lane still at -inf must not form -inf - -inf)
+      const float m_ref = grow ? mb_c : m_run;
+      const float alpha = grow ? ex2(m_run - m_ref) : 1.0f;  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_run = m_ref;
+    }
+    const float bias = (rowsel && m_run != -INFINITY) ? m_run : INFINITY;
     float ls = 0.f;
     bf16x8u pb[4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const __bf16 p = f32_to_bf16(ex2(st[h2][i] - m_use));
-        ls += (float)p;
-        pb[2 * h2 + i / 8][i % 8] = p;
+        const float p = ex2(fmaf(st[h2][i], qscale, -bias));
+        ls += p;
+        pb[2 * h2 + i / 8][i % 8] = (__bf16)p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    l_run += ls;
     // O^T += V^T P^T over 4 k-steps of 16 keys; slot 8*lh + e of k-step u
     // holds key 16*u + 8*(e/4) + 4*lh + (e%4).
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (16 * u < kc) {
+      if (!PKM || 16 * u < kc) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const uint16_t* vrow = &sm.vt[(32 * db + lr) * Sm::VS + 16 * u + 4 * lh];
@@ -266,6 +285,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       }
     }
   };
+  using kFull = std::integral_constant<bool, false>;
+  using kMasked = std::integral_constant<bool, true>;
 
   const int nkb_cube = (g.S + UKB - 1) / UKB;
   const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.N * D;
@@ -280,7 +301,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       __syncthreads();
       stage();
       __syncthreads();
-      if (wave_has_rows) compute(row_ok, kc, false, 0);
+      if (wave_has_rows) {
+        if (kc == UKB) compute(kFull{}, row_ok, kc, false, 0);
+        else compute(kMasked{}, row_ok, kc, false, 0);
+      }
     }
   }
   // ---- causal text keys (extra rows of a text prefill), chunk 0 --------------------------
@@ -296,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       stage();
       __syncthreads();
       const bool any = __ballot(row_ok && pos >= tb * UKB) != 0;
-      if (any) compute(row_ok && pos >= tb * UKB, kc, true, tb * UKB);
+      if (any) compute(kMasked{}, row_ok && pos >= tb * UKB, kc, true, tb * UKB);
     }
   }
 
@@ -384,7 +408,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
         fetch(kg + off2, vg + off2, D, min(UKB, g.S - kb2 * UKB));
       }
       const uint32_t mw = sm.bits[4 * ul + wave];
-      if (mw != 0u) compute(((mw >> lr) & 1u) != 0u, kc, false, 0);
+      if (mw != 0u) {
+        const bool sel = ((mw >> lr) & 1u) != 0u;
+        if (kc == UKB) compute(kFull{}, sel, kc, false, 0);
+        else compute(kMasked{}, sel, kc, false, 0);
+      }
     }
   }
 
@@ -420,11 +448,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[db][4 * q] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(acc[db][4 * q + 1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[db][4 * q + 2] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(acc[db][4 * q + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * q + 4 * lh) = make_uint2(w0, w1);
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[db][4 * q + e] * inv);
+      *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * q + 4 * lh) = o4;
     }
 }
 

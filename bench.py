@@ -48,6 +48,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--decode-batch", type=int, default=1,
                     help="decode tokens per step for the decode workload (1 = one step)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (for scaling "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -168,6 +171,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 3}))
+        return
     import workloads
     from adaptive_cube_sparse_amd import AdasAttention, Geometry
 
