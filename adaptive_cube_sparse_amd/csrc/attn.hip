@@ -574,7 +574,6 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_video_ro
 // host side
 // ---------------------------------------------------------------------------
 namespace {
-int attn_tr(const AttnArgs&) { return 128; }
 
 // The union-tile kernel (attn_union.hip) is the default bf16 path; the
 // gathered-row kernel in this file is kept for comparison and selected with
@@ -586,6 +585,9 @@ bool use_gather_kernel() {
   }();
   return v != 0;
 }
+
+// rows per tile of the active bf16 kernel (sets the split-partials layout)
+int attn_tr(const AttnArgs&) { return use_gather_kernel() ? 128 : union_tile_rows(); }
 }  // namespace
 
 void plan_attention(AttnArgs& a, adas_dtype dt) {
@@ -650,11 +652,12 @@ hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s) {
       sc.extra_chunk_cubes = a.extra_chunk_cubes;
       sc.n_extra_wgs = a.g.Hkv * sc.extra_tiles_per_group * sc.extra_chunks;
       const int n_tiles = a.g.Hkv * sc.extra_tiles_per_group;
-      const int waves = n_tiles * 128;
+      constexpr int TRU = 256;  // union_tile_rows()
+      const int waves = n_tiles * TRU;
       if (a.g.D == 128)
-        hipLaunchKernelGGL((k_merge_bf16<128, 128>), dim3((waves + 3) / 4), dim3(256), 0, s, a, sc, n_tiles);
+        hipLaunchKernelGGL((k_merge_bf16<128, TRU>), dim3((waves + 3) / 4), dim3(256), 0, s, a, sc, n_tiles);
       else
-        hipLaunchKernelGGL((k_merge_bf16<64, 128>), dim3((waves + 3) / 4), dim3(256), 0, s, a, sc, n_tiles);
+        hipLaunchKernelGGL((k_merge_bf16<64, TRU>), dim3((waves + 3) / 4), dim3(256), 0, s, a, sc, n_tiles);
       e = hipGetLastError();
     }
     return e;

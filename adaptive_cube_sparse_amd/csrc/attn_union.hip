@@ -1,20 +1,23 @@
 // Attention over the selected cubes plus the own cube (AdaSpark,
-// papernotes.org, key design 2) -- bf16 MFMA kernel, union tiles.
+// papernotes.org, key design 2: attend to the Top-p cube set and always keep
+// full attention to the own cube; one exact softmax, scale 1/sqrt(d_k)).
+// bf16 MFMA kernel with union tiles.
 //
-// A workgroup (4 waves) owns a tile of 128 rows that read the same KV head
-// (video rows of one query cube, or extra rows).  Each wave owns 32 rows; its
-// query block and its output accumulators stay in registers for the whole
-// tile.  The workgroup walks the union of its rows' selected cubes (plus the
-// own cube, or the causal text keys), one key block of 64 keys at a time:
-//   * K and V of the block are staged in LDS (V transposed), the next block is
-//     fetched into registers meanwhile;
-//   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, masks
-//     keys of cubes its row did not select (a bit per row and cube, built from
-//     the selection lists), runs the online softmax in float32 and
-//     accumulates O^T += V^T P^T; a wave none of whose rows selected the cube
-//     skips the block.
-// Rows therefore spend MFMA work on every key block of the tile union; the
-// masked part is the price of keeping accumulators in registers.
+// A workgroup (8 waves) owns a tile of 256 rows that read the same KV head
+// (video rows of one query cube, or extra rows).  Each wave owns 32 rows; their
+// query operands and float32 output accumulators stay in registers for the
+// whole tile.  The workgroup walks the union of its rows' selected cubes (plus
+// the own cube, or the causal text keys), one key block of 64 keys at a time:
+//   * K and V of a block are staged in LDS (V transposed) in one of two
+//     buffers; block i+1 is fetched into registers and staged while block i is
+//     computed, so each block costs one barrier;
+//   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, applies a
+//     per-row selection bit (row x cube bitmap built from the selection lists)
+//     as a +inf softmax bias, keeps the online softmax in log2 units with lazy
+//     rescaling, and accumulates O^T += V^T P^T.  A wave none of whose rows
+//     selected the cube skips the block.
+// Rows spend MFMA work on every key block of the tile union; the masked part is
+// the price of keeping accumulators in registers.
 //
 // Tile order: extra rows first (heaviest), then video tiles by descending
 // query cube.  When 8 is a multiple of the KV head count, workgroup b runs on
@@ -27,16 +30,22 @@
 namespace adas {
 
 typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4u __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 constexpr int UKB = 64;      // keys per key block
-constexpr int UTR = 128;     // rows per tile
+constexpr int UNW = 8;       // waves per workgroup
+constexpr int UNT = 64 * UNW;
+constexpr int UTR = 32 * UNW;  // rows per tile
 constexpr int UPASS = 1024;  // cubes per selection-bitmap pass
 constexpr float kLog2eU = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;  // rescale only when a block max exceeds the reference by 2^8
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 }  // namespace
+
+int union_tile_rows() { return UTR; }
 
 struct USched {
   int video_tiles_per_group;
@@ -49,17 +58,17 @@ struct USched {
 
 template <int D>
 struct USmem {
-  static constexpr int KS = D + 8;    // bf16 stride of a K row
+  static constexpr int KS = D + 8;    // bf16 stride of a K row (68 dwords: conflict-free b128 reads)
   static constexpr int VS = UKB + 4;  // bf16 stride of a V^T row (34 dwords: conflict-free b64 reads)
-  uint16_t k[UKB * KS];
-  uint16_t vt[D * VS];
-  uint32_t bits[UPASS * 4];  // [cube in pass][wave] -> rows of the wave that selected it
-  uint16_t ulist[UPASS];     // cubes of the pass selected by any row
+  uint16_t k[2][UKB * KS];
+  uint16_t vt[2][D * VS];
+  uint32_t bits[UPASS * UNW];  // [cube in pass][wave] -> rows of the wave that selected it
+  uint16_t ulist[UPASS];       // cubes of the pass selected by any row
   int n_union;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
+__global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using Sm = USmem<D>;
   __shared__ Sm sm;
   const KGeom& g = a.g;
@@ -146,84 +155,70 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  // ---- K/V staging: 4 x 16 B of K and V per thread (D = 128) --------------------------
-  constexpr int VPR = D / 8;                    // 16-byte vectors per row
-  constexpr int NV = UKB * VPR / 256;           // vectors per thread (4 or 2)
-  uint4 kr[NV], vr[NV];
-  // K: vector e = tid + 256*u -> key e / VPR, chunk e % VPR (row-major copy).
-  // V: thread owns keys 4*kq .. 4*kq+3 of d-chunk vc, transposed on store.
-  // d-chunk handled by V-staging thread group q: bits 0 and 1 swapped, so the
-  // two 16-lane groups of a 32-lane half write V^T rows 2 chunks apart.
-  auto vchunk_of = [](int q) { return (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1); };
-  auto fetch = [&](const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) {
+  // ---- K/V staging --------------------------------------------------------------------
+  // K: 16-byte vector e = tid + UNT*u -> key e / VPR, chunk e % VPR (row-major copy).
+  // V: thread (key pair kp, d-chunk vc) loads keys 2kp, 2kp+1 and writes V^T
+  //    rows 8vc..8vc+7 as 32-bit pairs.  The two lane halves of a wave take
+  //    d-chunks two apart, so a 64-lane store covers 64 distinct banks.
+  constexpr int VPR = D / 8;
+  constexpr int NK = UKB * VPR / UNT;  // K vectors per thread (2 for D = 128, 1 for D = 64)
+  const int kp = lane & 31;
+  const int vc = 4 * (wave >> 1) + (wave & 1) + 2 * lh;
+  const bool v_thread = vc < VPR;
+  uint4 kr[NK], vr[2];
+  auto fetch = [&](const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = tid + 256 * u;
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + UNT * u;
       const int key = e / VPR, ch = e % VPR;
       kr[u] = key < kc ? *reinterpret_cast<const uint4*>(kb + key * stride + ch * 8)
                        : make_uint4(0, 0, 0, 0);
     }
-    // V: NV keys (4 for D=128, 2 for D=64) per thread
-    constexpr int KQ = UKB / 4;  // 16 key quads
-    const int kq = tid % KQ, vc = vchunk_of(tid / KQ);  // vc < 256/16 = 16 d-chunks
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int key = (NV == 4 ? 4 * kq + u : 4 * kq + 2 * (vc / VPR) + u);
-      const int chv = vc % VPR;
-      vr[u] = key < kc ? *reinterpret_cast<const uint4*>(vb + key * stride + chv * 8)
-                       : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int key = 2 * kp + u;
+      vr[u] = (v_thread && key < kc) ? *reinterpret_cast<const uint4*>(vb + key * stride + vc * 8)
+                                     : make_uint4(0, 0, 0, 0);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = tid + 256 * u;
+    for (int u = 0; u < NK; ++u) {
+      const int e = tid + UNT * u;
       const int key = e / VPR, ch = e % VPR;
-      *reinterpret_cast<uint4*>(&sm.k[key * Sm::KS + ch * 8]) = kr[u];
+      *reinterpret_cast<uint4*>(&sm.k[buf][key * Sm::KS + ch * 8]) = kr[u];
     }
-    constexpr int KQ = UKB / 4;
-    const int kq = tid % KQ, vc = vchunk_of(tid / KQ);
-    const int chv = vc % VPR;
-    const int key0 = NV == 4 ? 4 * kq : 4 * kq + 2 * (vc / VPR);
-    // transpose: element (key0+u, 8*chv+e) -> vt[8*chv+e][key0+u]
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(vr);
+    if (v_thread) {
+      const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+      const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t h[NV];
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const uint32_t word = w[u * 4 + e / 2];
-        h[u] = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
-      }
-      uint16_t* dst = &sm.vt[(8 * chv + e) * Sm::VS + key0];
-      if constexpr (NV == 4) {
-        *reinterpret_cast<uint2*>(dst) =
-            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (e & 1) ? (w0[e / 2] >> 16) : (w0[e / 2] & 0xFFFFu);
+        const uint32_t hi = (e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16);
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][(8 * vc + e) * Sm::VS + 2 * kp]) = lo | hi;
       }
     }
   };
 
-  // ---- one key block: rowsel = this lane's row takes part --------------------------
+  // ---- one key block from buffer `buf`: rowsel = this lane's row takes part --------
   // kc valid keys; causal: key kbase_idx + key must be <= the row's token index.
-  // Scores stay in log2 units (qscale folds 1/sqrt(d) and log2 e).  The running
-  // reference m_run is raised only when a block's max exceeds it by more than
-  // kLazy (P <= 2^kLazy meanwhile), so the accumulators are rescaled rarely.
   // A lane whose row did not select the block gets bias +inf, i.e. P = 0.
-  constexpr float kLazy = 8.0f;
-  auto compute = [&](auto per_key_mask, bool rowsel, int kc, bool causal, int kbase_idx) {
+  auto compute = [&](auto per_key_mask, int buf, bool rowsel, int kc, bool causal, int kbase_idx) __attribute__((always_inline)) {
     constexpr bool PKM = decltype(per_key_mask)::value;
+    const uint16_t* kbuf = sm.k[buf];
+    const uint16_t* vbuf = sm.vt[buf];
     f32x16 st[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[h2][i] = 0.f;
-      if (!PKM || 32 * h2 < kc) {
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) {
+    for (int ds = 0; ds < D / 16; ++ds) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        if (!PKM || 32 * h2 < kc) {
           const bf16x8u ka = __builtin_bit_cast(
-              bf16x8u, *reinterpret_cast<const uint4*>(&sm.k[(32 * h2 + lr) * Sm::KS + 16 * ds + 8 * lh]));
+              bf16x8u, *reinterpret_cast<const uint4*>(&kbuf[(32 * h2 + lr) * Sm::KS + 16 * ds + 8 * lh]));
           st[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ds], st[h2], 0, 0, 0);
         }
       }
@@ -247,14 +242,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
     const bool grow = mb_c > m_run + kLazy;
     if (__ballot(grow) != 0ull) {
       // only growing lanes rescale (a lane still at -inf must not form -inf - -inf)
-      const float m_ref = grow ? mb_c : m_run;
-      const float alpha = grow ? ex2(m_run - m_ref) : 1.0f;  // 0 when m_run = -inf
+      const float alpha = grow ? ex2(m_run - mb_c) : 1.0f;  // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m_run = m_ref;
+      m_run = grow ? mb_c : m_run;
     }
     const float bias = (rowsel && m_run != -INFINITY) ? m_run : INFINITY;
     float ls = 0.f;
@@ -276,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       if (!PKM || 16 * u < kc) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* vrow = &sm.vt[(32 * db + lr) * Sm::VS + 16 * u + 4 * lh];
+          const uint16_t* vrow = &vbuf[(32 * db + lr) * Sm::VS + 16 * u + 4 * lh];
           const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
           const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
           const bf16x8u va = __builtin_bit_cast(bf16x8u, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -288,40 +282,72 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
   using kFull = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
 
+  // Pipelined walk over nb key blocks: source(i, kptr, vptr, stride, kc) names
+  // block i, work(i, buf, kc) computes it.  One barrier per block: staging
+  // into buffer i&1 is safe because every wave finished block i-2 before the
+  // barrier of block i-1.
+  auto pipeline = [&](int nb, auto source, auto work) __attribute__((always_inline)) {
+    if (nb <= 0) return;
+    __syncthreads();  // the previous phase no longer reads either buffer
+    const uint16_t *kp0, *vp0;
+    size_t st0;
+    int kc0;
+    source(0, kp0, vp0, st0, kc0);
+    fetch(kp0, vp0, st0, kc0);
+    int kc_cur = kc0;
+    for (int i = 0; i < nb; ++i) {
+      const int buf = i & 1;
+      stage(buf);
+      int kc_next = 0;
+      if (i + 1 < nb) {
+        const uint16_t *kpn, *vpn;
+        size_t stn;
+        source(i + 1, kpn, vpn, stn, kc_next);
+        fetch(kpn, vpn, stn, kc_next);
+      }
+      __syncthreads();
+      work(i, buf, kc_cur);
+      kc_cur = kc_next;
+    }
+  };
+
   const int nkb_cube = (g.S + UKB - 1) / UKB;
   const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.N * D;
   const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.N * D;
 
   // ---- own cube (video): every row ------------------------------------------------------
   if (video) {
-    for (int kb = 0; kb < nkb_cube; ++kb) {
-      const int kc = min(UKB, g.S - kb * UKB);
-      const size_t off = ((size_t)c * g.S + kb * UKB) * D;
-      fetch(kg + off, vg + off, D, kc);
-      __syncthreads();
-      stage();
-      __syncthreads();
-      if (wave_has_rows) {
-        if (kc == UKB) compute(kFull{}, row_ok, kc, false, 0);
-        else compute(kMasked{}, row_ok, kc, false, 0);
-      }
-    }
+    pipeline(
+        nkb_cube,
+        [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
+          const size_t off = ((size_t)c * g.S + i * UKB) * D;
+          kp_ = kg + off;
+          vp_ = vg + off;
+          st_ = D;
+          kc_ = min(UKB, g.S - i * UKB);
+        },
+        [&](int, int buf, int kc) __attribute__((always_inline)) {
+          if (!wave_has_rows) return;
+          if (kc == UKB) compute(kFull{}, buf, row_ok, kc, false, 0);
+          else compute(kMasked{}, buf, row_ok, kc, false, 0);
+        });
   }
   // ---- causal text keys (extra rows of a text prefill), chunk 0 --------------------------
   if (!video && a.n_text_kv > 0 && chunk == 0) {
     const uint16_t* kt = (const uint16_t*)a.k_text + (size_t)grp * D;
     const uint16_t* vt = (const uint16_t*)a.v_text + (size_t)grp * D;
-    const int ntb = (a.n_text_kv + UKB - 1) / UKB;
-    for (int tb = 0; tb < ntb; ++tb) {
-      const int kc = min(UKB, a.n_text_kv - tb * UKB);
-      fetch(kt + (size_t)tb * UKB * g.Hkv * D, vt + (size_t)tb * UKB * g.Hkv * D,
-            (size_t)g.Hkv * D, kc);
-      __syncthreads();
-      stage();
-      __syncthreads();
-      const bool any = __ballot(row_ok && pos >= tb * UKB) != 0;
-      if (any) compute(kMasked{}, row_ok && pos >= tb * UKB, kc, true, tb * UKB);
-    }
+    pipeline(
+        (a.n_text_kv + UKB - 1) / UKB,
+        [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
+          kp_ = kt + (size_t)i * UKB * g.Hkv * D;
+          vp_ = vt + (size_t)i * UKB * g.Hkv * D;
+          st_ = (size_t)g.Hkv * D;
+          kc_ = min(UKB, a.n_text_kv - i * UKB);
+        },
+        [&](int i, int buf, int kc) __attribute__((always_inline)) {
+          const bool sel = row_ok && pos >= i * UKB;
+          if (__ballot(sel) != 0ull) compute(kMasked{}, buf, sel, kc, true, i * UKB);
+        });
   }
 
   // ---- selected cubes -----------------------------------------------------------------
@@ -360,11 +386,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
   for (int jb = cube_lo; jb < cube_hi; jb += UPASS) {
     const int je = min(cube_hi, jb + UPASS);
     const int span = je - jb;
-    __syncthreads();  // previous users of bits/ulist/LDS are done
-    for (int e = tid; e < span * 4; e += 256) sm.bits[e] = 0u;
+    __syncthreads();  // previous users of bits/ulist are done
+    for (int e = tid; e < span * UNW; e += UNT) sm.bits[e] = 0u;
     __syncthreads();
     if (my_row < n_rows) {
-      // entries in [jb, je): binary search for both ends (lists ascending)
+      // entries in [jb, je): binary search for both ends (lists are ascending)
       int lo = 0, hi = my_cnt;
       while (lo < hi) { const int mid = (lo + hi) >> 1; if (my_list[mid] < jb) lo = mid + 1; else hi = mid; }
       int lo2 = lo, hi2 = my_cnt;
@@ -372,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       const uint32_t bit = 1u << (my_row & 31);
       uint32_t* wbase = &sm.bits[my_row >> 5];
 #pragma unroll 4
-      for (int i = lo + my_half; i < lo2; i += 2) atomicOr(wbase + 4 * (my_list[i] - jb), bit);
+      for (int i = lo + my_half; i < lo2; i += 2) atomicOr(wbase + UNW * (my_list[i] - jb), bit);
     }
     __syncthreads();
     if (wave == 0) {
@@ -380,7 +406,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       for (int u0 = 0; u0 < span; u0 += 64) {
         const int u = u0 + lane;
         bool any = false;
-        if (u < span) any = (sm.bits[4 * u] | sm.bits[4 * u + 1] | sm.bits[4 * u + 2] | sm.bits[4 * u + 3]) != 0u;
+        if (u < span) {
+          uint32_t o = 0;
+#pragma unroll
+          for (int w = 0; w < UNW; ++w) o |= sm.bits[UNW * u + w];
+          any = o != 0u;
+        }
         const uint64_t bal = __ballot(any);
         if (any) sm.ulist[base + lanes_below(bal)] = (uint16_t)u;
         base += popc64(bal);
@@ -388,32 +419,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
       if (lane == 0) sm.n_union = base;
     }
     __syncthreads();
-    const int nblocks = sm.n_union * nkb_cube;
-    if (nblocks == 0) continue;
-    {
-      const int j = jb + sm.ulist[0];
-      fetch(kg + (size_t)j * g.S * D, vg + (size_t)j * g.S * D, D, min(UKB, g.S));
-    }
-    for (int it = 0; it < nblocks; ++it) {
-      const int ci = it / nkb_cube, kb = it - ci * nkb_cube;
-      const int ul = sm.ulist[ci];
-      const int kc = min(UKB, g.S - kb * UKB);
-      __syncthreads();  // LDS K/V free
-      stage();
-      __syncthreads();
-      if (it + 1 < nblocks) {
-        const int ci2 = (it + 1) / nkb_cube, kb2 = (it + 1) - ci2 * nkb_cube;
-        const int j2 = jb + sm.ulist[ci2];
-        const size_t off2 = ((size_t)j2 * g.S + kb2 * UKB) * D;
-        fetch(kg + off2, vg + off2, D, min(UKB, g.S - kb2 * UKB));
-      }
-      const uint32_t mw = sm.bits[4 * ul + wave];
-      if (mw != 0u) {
-        const bool sel = ((mw >> lr) & 1u) != 0u;
-        if (kc == UKB) compute(kFull{}, sel, kc, false, 0);
-        else compute(kMasked{}, sel, kc, false, 0);
-      }
-    }
+    pipeline(
+        sm.n_union * nkb_cube,
+        [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
+          const int ci = i / nkb_cube, kb = i - ci * nkb_cube;
+          const int j = jb + sm.ulist[ci];
+          const size_t off = ((size_t)j * g.S + kb * UKB) * D;
+          kp_ = kg + off;
+          vp_ = vg + off;
+          st_ = D;
+          kc_ = min(UKB, g.S - kb * UKB);
+        },
+        [&](int i, int buf, int kc) __attribute__((always_inline)) {
+          const int ul = sm.ulist[i / nkb_cube];
+          const uint32_t mw = sm.bits[UNW * ul + wave];
+          if (mw == 0u) return;
+          const bool sel = ((mw >> lr) & 1u) != 0u;
+          if (kc == UKB) compute(kFull{}, buf, sel, kc, false, 0);
+          else compute(kMasked{}, buf, sel, kc, false, 0);
+        });
   }
 
   // ---- epilogue ----------------------------------------------------------------------
@@ -448,11 +472,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_union(AttnArgs a, USched sc) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 o4;
+      bf16x4u o4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[db][4 * q + e] * inv);
-      *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * q + 4 * lh) = o4;
+      *reinterpret_cast<bf16x4u*>(dst + 32 * db + 8 * q + 4 * lh) = o4;
     }
 }
 
@@ -476,7 +499,7 @@ hipError_t launch_union(const AttnArgs& a, hipStream_t s) {
   }
   const long blocks = sc.n_extra_wgs + video_blocks;
   if (blocks > 0)
-    hipLaunchKernelGGL((k_attn_union<D>), dim3((unsigned)blocks), dim3(256), 0, s, a, sc);
+    hipLaunchKernelGGL((k_attn_union<D>), dim3((unsigned)blocks), dim3(UNT), 0, s, a, sc);
   return hipGetLastError();
 }
 

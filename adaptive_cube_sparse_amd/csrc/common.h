@@ -244,5 +244,6 @@ size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt);
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s);
 template <int D>
 hipError_t launch_union(const AttnArgs& a, hipStream_t s);
+int union_tile_rows();  // rows per tile of the union kernel
 
 }  // namespace adas
