@@ -59,6 +59,8 @@ class AdasAttention:
         self.sel_idx = torch.empty((max(cap, 1),), device=dev, dtype=torch.int32)
         wsb = adas_workspace_bytes(g, dtype, ADAS_WS_ATTN, has_video, n_extra)
         self.ws = torch.empty((max(wsb, 1),), device=dev, dtype=torch.uint8) if wsb else None
+        wss = adas_workspace_bytes(g, dtype, ADAS_WS_SELECT, has_video, n_extra)
+        self.ws_select = torch.empty((wss,), device=dev, dtype=torch.uint8) if wss else None
 
     # -- steps ---------------------------------------------------------------
     def build_kv(self, k_raster: torch.Tensor, v_raster: torch.Tensor, stream=None):
@@ -73,7 +75,7 @@ class AdasAttention:
 
     def select(self, q_extra: Optional[torch.Tensor] = None, p: Optional[float] = None, stream=None):
         adas_select_topp(self.geom, self.q_cube, q_extra, self.kbar, self.p if p is None else p,
-                         self.sel_count, self.sel_idx, None, stream)
+                         self.sel_count, self.sel_idx, self.ws_select, stream)
 
     def attend(self, q_extra=None, k_text=None, v_text=None, stream=None):
         adas_sparse_attn_fwd(self.geom, self.q_cube, self.k_cube, self.v_cube, q_extra, k_text, v_text,

@@ -136,8 +136,6 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
                              int32_t n_extra, const void* q_extra, const float* kbar, float p,
                              int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
                              size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;  // the selection keeps its logits in LDS; no workspace
   adas::KGeom g;
   adas::HeadGroups hg;
   adas_status st = derive(geom, g, hg);
@@ -156,8 +154,12 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
   if (sel_cap < need)
     return fail(ADAS_ERR_CAPACITY, "sel_cap %lld < required %lld", (long long)sel_cap,
                 (long long)need);
+  const size_t ws_need = adas::select_workspace_bytes(g, dtype);
+  if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need))
+    return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_need);
   adas::SelectArgs a;
   a.g = g;
+  a.kbar_split = ws;
   a.hg = hg;
   a.q_cube = q_cube;
   a.q_extra = q_extra;
@@ -226,7 +228,12 @@ adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const 
 
 size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kind kind,
                             int32_t has_video, int32_t n_extra) {
-  if (kind == ADAS_WS_SELECT) return 0;  // logits stay in LDS
+  if (kind == ADAS_WS_SELECT) {
+    adas::KGeom g;
+    adas::HeadGroups hg;
+    if (derive(geom, g, hg) != ADAS_OK || check_dtype(dtype) != ADAS_OK) return 0;
+    return adas::select_workspace_bytes(g, dtype);
+  }
   adas::AttnArgs a;
   const int dummy = 1;
   if (build_attn(geom, dtype, has_video ? &dummy : nullptr, n_extra, 0, a) != ADAS_OK) return 0;

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     float mb = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
     for (int i = 1; i < 16; ++i) mb = fmaxf(mb, fmaxf(st[0][i], st[1][i]));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    mb = fmaxf(mb, xor32_f32(mb));
     const float mb_c = rowsel ? mb * qscale : -INFINITY;
     const bool grow = mb_c > m_run + kLazy;
     if (__ballot(grow) != 0ull) {
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         ls += p;
         pb[2 * h2 + i / 8][i % 8] = (__bf16)p;
       }
-    ls += __shfl_xor(ls, 32, 64);
+    ls += xor32_f32(ls);
     l_run += ls;
     // O^T += V^T P^T over 4 k-steps of 16 keys; slot 8*lh + e of k-step u
     // holds key 16*u + 8*(e/4) + 4*lh + (e%4).

@@ -75,19 +75,40 @@ __device__ __forceinline__ __bf16 f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions.  The xor butterfly gives bit-identical results on every
-// lane (each step adds the same two operands on both partners), so decisions
-// taken on the result are wave-uniform.
+// wave64 reductions on DPP (no LDS traffic).  quad_perm, row_half_mirror and
+// row_mirror fold each 16-lane row; row_bcast15 / row_bcast31 carry rows 0-2
+// into row 3; lane 63 then holds the total, and readlane makes the result one
+// wave-uniform scalar, so decisions taken on it are uniform.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+__device__ __forceinline__ float wave_sum(float t) {
+  t += dpp_f32<0xb1>(t, 0.f);        // quad_perm [1,0,3,2]
+  t += dpp_f32<0x4e>(t, 0.f);        // quad_perm [2,3,0,1]
+  t += dpp_f32<0x141>(t, 0.f);       // row_half_mirror
+  t += dpp_f32<0x140>(t, 0.f);       // row_mirror
+  t += dpp_f32<0x142, 0xa>(t, 0.f);  // row_bcast15 -> rows 1, 3
+  t += dpp_f32<0x143, 0xc>(t, 0.f);  // row_bcast31 -> rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 63));
+}
+__device__ __forceinline__ float wave_max(float t) {
+  t = fmaxf(t, dpp_f32<0xb1>(t, -INFINITY));
+  t = fmaxf(t, dpp_f32<0x4e>(t, -INFINITY));
+  t = fmaxf(t, dpp_f32<0x141>(t, -INFINITY));
+  t = fmaxf(t, dpp_f32<0x140>(t, -INFINITY));
+  t = fmaxf(t, dpp_f32<0x142, 0xa>(t, -INFINITY));
+  t = fmaxf(t, dpp_f32<0x143, 0xc>(t, -INFINITY));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 63));
+}
+// value of lane (lane ^ 32), via v_permlane32_swap
+__device__ __forceinline__ float xor32_f32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? (unsigned)r[0] : (unsigned)r[1]);
 }
 __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
 // number of set bits of m in lanes below this one
@@ -104,17 +125,24 @@ __device__ __forceinline__ float fast_exp(float x) {
 // Top-p on one row held by one wave (key design 2, the S_i equation).
 //
 // E[i] (lane L) is exp(z_j - max z) for candidate j = L + 64*i, or -1 for
-// j >= n (padding).  Z is the wave-uniform sum of the valid E.  Finds the
-// Top-p set under the order (E descending, j ascending) and writes its ids
-// ascending to out[0..count).  Returns count (wave-uniform).
+// j >= n (padding), with n <= 64*NPL.  Z is the wave-uniform sum of the valid
+// E.  Finds the Top-p set under the order (E descending, j ascending), writes
+// its ids ascending to out[0..count) and returns count (wave-uniform).
+// `scratch` is 64 floats of LDS private to the wave.
 //
 // Method: the selected set is {E > tau} plus the lowest-index ties at tau,
-// where tau is the largest float with mass(E >= tau) >= p*Z.  tau is found
-// by bisection on the float bit pattern (positive floats order like their
-// bits), stopping as soon as one element is left between the bounds.
+// where tau is the largest float with mass(E >= tau) >= p*Z.  tau is found by
+// bisection on the float bit pattern (positive floats order like their bits):
+//   1. on all candidates until at most 64 lie between the bounds [lo, hi);
+//   2. those are gathered one per lane, the mass at or above hi is fixed, and
+//      the bisection continues on single registers until one element (or one
+//      bit pattern) is left.
+// The loops are fully unrolled and branch-free over NPL, so NPL should be the
+// smallest capacity that holds n.
 // ---------------------------------------------------------------------------
 template <int NPL>
-__device__ int topp_select_row(float (&E)[NPL], int n, float Z, float p, int32_t* __restrict__ out) {
+__device__ int topp_select_row(const float (&E)[NPL], int n, float Z, float p,
+                               int32_t* __restrict__ out, float* __restrict__ scratch) {
   const int lane = threadIdx.x & (kWave - 1);
   if (n <= 0) return 0;
   if (p >= 1.0f) {
@@ -124,22 +152,10 @@ __device__ int topp_select_row(float (&E)[NPL], int n, float Z, float p, int32_t
   const float target = p * Z;
   uint32_t lo = 0u, hi = 0x3F800001u;  // mass(E >= lo) >= target > mass(E >= hi)
   int cnt_lo = n, cnt_hi = 0;
-  float tau;
-  for (;;) {
-    if (cnt_lo - cnt_hi == 1) {
-      // exactly one element in [lo, hi): it is the cut element
-      float best = -1.0f;
-      const float fhi = __uint_as_float(hi);
-#pragma unroll
-      for (int i = 0; i < NPL; ++i)
-        if (E[i] >= __uint_as_float(lo) && E[i] < fhi) best = fmaxf(best, E[i]);
-      tau = wave_max(best);
-      break;
-    }
-    if (hi - lo <= 1u) {
-      tau = __uint_as_float(lo);
-      break;
-    }
+  float tau = 0.0f;
+  bool found = false;
+  // 1. full bisection
+  while (cnt_lo - cnt_hi > kWave && hi - lo > 1u) {
     const uint32_t mid = lo + ((hi - lo) >> 1);
     const float fm = __uint_as_float(mid);
     float ms = 0.0f;
@@ -157,6 +173,52 @@ __device__ int topp_select_row(float (&E)[NPL], int n, float Z, float p, int32_t
     } else {
       hi = mid;
       cnt_hi = cnt;
+    }
+  }
+  if (hi - lo <= 1u) {
+    tau = __uint_as_float(lo);
+    found = true;
+  }
+  if (!found) {
+    // 2. fixed mass at or above hi; gather the (<= 64) elements in [lo, hi)
+    const float flo = __uint_as_float(lo), fhi = __uint_as_float(hi);
+    float mhi = 0.0f;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      mhi += E[i] >= fhi ? E[i] : 0.0f;
+      const bool in = E[i] >= flo && E[i] < fhi;
+      const uint64_t b = __ballot(in);
+      if (in) scratch[base + lanes_below(b)] = E[i];
+      base += popc64(b);
+    }
+    mhi = wave_sum(mhi);
+    __builtin_amdgcn_wave_barrier();
+    const float v = lane < base ? scratch[lane] : -1.0f;
+    // 3. bisection on one value per lane; every gathered v is below the
+    //    gather-time bound, whose mass (mhi) and count (cnt_hi0) stay fixed
+    const int cnt_hi0 = cnt_hi;
+    for (;;) {
+      if (cnt_lo - cnt_hi == 1) {  // exactly one element in [lo, hi): the cut
+        tau = wave_max(v >= __uint_as_float(lo) && v < __uint_as_float(hi) ? v : -1.0f);
+        break;
+      }
+      if (hi - lo <= 1u) {
+        tau = __uint_as_float(lo);
+        break;
+      }
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      const float fm = __uint_as_float(mid);
+      const bool ge = v >= fm;
+      const int cnt = cnt_hi0 + popc64(__ballot(ge));
+      const float ms = mhi + wave_sum(ge ? v : 0.0f);
+      if (ms >= target) {
+        lo = mid;
+        cnt_lo = cnt;
+      } else {
+        hi = mid;
+        cnt_hi = cnt;
+      }
     }
   }
   // mass strictly above tau and the number of ties at tau
@@ -205,6 +267,7 @@ struct SelectArgs {
   const void* q_cube;   // may be null
   const void* q_extra;  // may be null
   const float* kbar;
+  void* kbar_split;  // workspace: three bf16 planes of kbar (bf16 path)
   int n_extra;
   float p;
   int32_t* sel_count;
@@ -214,6 +277,7 @@ struct SelectArgs {
   int has_video;
 };
 hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s);
+size_t select_workspace_bytes(const KGeom& g, adas_dtype dt);
 
 struct AttnArgs {
   KGeom g;

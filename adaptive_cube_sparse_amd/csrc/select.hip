@@ -2,16 +2,20 @@
 // 2: P_i = softmax_j(q . kbar_j / sqrt(d_k)) over the preceding cubes,
 // S_i = Top-p(P_i, p); key design 4: one threshold p).
 //
-// bf16 path.  A workgroup (4 waves) owns a tile of RT rows that share a KV
+// bf16 path.  A workgroup (8 waves) owns a tile of RT rows that share a KV
 // head and a candidate count n (video rows of one query cube, or extra rows).
 //   phase A  scores: z = Q_tile x kbar^T on MFMA (v_mfma_f32_16x16x32_bf16).
-//            kbar is float32; it is split into hi + mid + lo bf16 parts so
-//            that three bf16 products reproduce float32 accuracy (rounding
-//            kbar to bf16 alone would move logits by ~1e-3).  Waves stride
-//            over 16-candidate blocks; logits land in LDS.
+//            Each float32 kbar chunk is split in registers into hi + mid + lo
+//            bf16 parts, so that three bf16 products reproduce float32
+//            accuracy (rounding kbar to bf16 alone would move logits by
+//            ~1e-3).  Waves stride over 16-candidate blocks, every kbar load
+//            serves all RT rows; logits land in LDS.
 //   phase B  per row (one wave): max, exp, sum, then the Top-p threshold
 //            search and ascending compaction of topp_select_row().
 // f32 path: one wave per row, float32 dot products on the vector ALUs.
+#include <algorithm>
+#include <utility>
+
 #include "common.h"
 
 namespace adas {
@@ -21,7 +25,8 @@ namespace {
 struct TileSched {
   int video_tiles_per_group;  // tiles per (kv head, query cube)
   int extra_tiles_per_group;
-  int n_extra_tiles;          // Hkv * extra_tiles_per_group
+  int n_extra_tiles;          // Hkv * extra_tiles_per_group (0 in launches without extra rows)
+  int c_lo, c_hi;             // video query cubes [c_lo, c_hi) served by this launch
 };
 
 // Row rho of a KV-head group -> (query head, position).  Video rows enumerate
@@ -65,32 +70,38 @@ __device__ __forceinline__ void decode_tile(int b, const TileSched& ts, int Hkv,
     video = true;
     b -= ts.n_extra_tiles;
     const int per_c = Hkv * ts.video_tiles_per_group;
-    c = Nc - 1 - b / per_c;
+    c = ts.c_hi - 1 - b / per_c;
     const int rem = b % per_c;
     grp = rem / ts.video_tiles_per_group;
     rho0 = (rem - grp * ts.video_tiles_per_group) * RT;
   }
 }
 
+}  // namespace
+
+// hi + mid + lo bf16 parts of 8 float32 values, so that three bf16 products
+// reproduce a float32 product: hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid) (each subtraction is exact in float32).
 __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const __bf16 h = f32_to_bf16(x[i]);
+    const __bf16 h = (__bf16)x[i];
     const float r1 = x[i] - (float)h;
-    const __bf16 m = f32_to_bf16(r1);
-    const float r2 = r1 - (float)m;
+    const __bf16 m = (__bf16)r1;
     hi[i] = h;
     mid[i] = m;
-    lo[i] = f32_to_bf16(r2);
+    lo[i] = (__bf16)(r1 - (float)m);
   }
 }
 
-}  // namespace
+constexpr int kSelWaves = 8;
 
-// RT rows per tile, NPL candidate slots per lane (capacity 64 * NPL).
+// RT rows per tile (a multiple of 16, or 8), NPL candidate slots per lane
+// (capacity 64 * NPL).  Eight waves share every kbar load across RT rows.
 template <int D, int RT, int NPL>
-__global__ __launch_bounds__(256) void k_select_bf16(SelectArgs a, TileSched ts) {
+__global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, TileSched ts) {
   constexpr int NCAP = kWave * NPL;
+  constexpr int RB = (RT + 15) / 16;  // 16-row MFMA blocks
   __shared__ float sZ[RT * NCAP];
   const KGeom& g = a.g;
   const int lane = threadIdx.x & (kWave - 1);
@@ -100,20 +111,19 @@ __global__ __launch_bounds__(256) void k_select_bf16(SelectArgs a, TileSched ts)
   bool video;
   decode_tile(blockIdx.x, ts, g.Hkv, g.Nc, RT, grp, n, rho0, video);
   // n == candidate count: c for a video row in cube c, Nc for extra rows.
+  const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
+  const int group_rows = video ? gsz * g.S : gsz * a.n_extra;
 
   // ---- phase A: scores --------------------------------------------------
-  // A operand: 16 query rows (rows >= RT are zero), lane -> row lane%16,
-  // k = 32*s + 8*(lane/16) + [0..7].
-  bf16x8 qa[D / 32];
-  {
-    const int i = lane % 16;
+  // A operand of row block rb: tile row 16*rb + lane%16 (rows beyond the tile
+  // are zero), k = 32*s + 8*(lane/16) + [0..7].
+  bf16x8 qa[RB][D / 32];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = 16 * rb + lane % 16;
     RowRef rr = {-1, 0, false};
-    if (i < RT) {
-      if (video) rr = video_row(a.hg, grp, n, g.S, rho0 + i);
-      else if (rho0 + i < (a.hg.start[grp + 1] - a.hg.start[grp]) * a.n_extra)
-        rr = extra_row(a.hg, grp, a.n_extra, rho0 + i);
-    }
-    if (video && rr.hq >= 0 && rho0 + i >= (a.hg.start[grp + 1] - a.hg.start[grp]) * g.S) rr.hq = -1;
+    if (i < RT && rho0 + i < group_rows)
+      rr = video ? video_row(a.hg, grp, n, g.S, rho0 + i) : extra_row(a.hg, grp, a.n_extra, rho0 + i);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       uint4 raw = make_uint4(0, 0, 0, 0);
@@ -123,16 +133,18 @@ __global__ __launch_bounds__(256) void k_select_bf16(SelectArgs a, TileSched ts)
             : (const uint16_t*)a.q_extra + ((size_t)rr.pos * g.Hq + rr.hq) * D;
         raw = *reinterpret_cast<const uint4*>(q + 32 * s + 8 * (lane / 16));
       }
-      qa[s] = __builtin_bit_cast(bf16x8, raw);
+      qa[rb][s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
   const float scale = 1.0f / sqrtf((float)D);
   const float* kb = a.kbar + (size_t)grp * g.Nc * D;
   const int nblk = (n + 15) / 16;
-  for (int blk = wave; blk < nblk; blk += 4) {
+  for (int blk = wave; blk < nblk; blk += kSelWaves) {
     const int j = blk * 16 + lane % 16;
     const int jj = j < n ? j : n - 1;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       const float4* src = reinterpret_cast<const float4*>(kb + (size_t)jj * D + 32 * s + 8 * (lane / 16));
@@ -140,33 +152,33 @@ __global__ __launch_bounds__(256) void k_select_bf16(SelectArgs a, TileSched ts)
       const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       bf16x8 hi, mid, lo;
       split3(x, hi, mid, lo);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], lo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], mid, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], hi, acc, 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb][s], lo, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb][s], mid, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb][s], hi, acc[rb], 0, 0, 0);
+      }
     }
-    // acc[i] = z for row 4*(lane/16)+i, candidate j
+    // acc[rb][i] = z for tile row 16*rb + 4*(lane/16) + i, candidate j
     if (j < n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * (lane / 16) + i;
-        if (row < RT) sZ[row * NCAP + j] = acc[i] * scale;
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rb + 4 * (lane / 16) + i;
+          if (row < RT) sZ[row * NCAP + j] = acc[rb][i] * scale;
+        }
     }
   }
   __syncthreads();
 
-  // ---- phase B: softmax + Top-p per row -----------------------------------
-  const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
-  for (int row = wave; row < RT; row += 4) {
+  // ---- phase B: softmax + Top-p, one row at a time per wave ------------------
+  // The row's LDS logits are dead once loaded, so they serve as the wave's
+  // 64-float scratch for the Top-p gather.
+  for (int row = wave; row < RT; row += kSelWaves) {
     const int rho = rho0 + row;
-    RowRef rr;
-    if (video) {
-      if (rho >= gsz * g.S) break;
-      rr = video_row(a.hg, grp, n, g.S, rho);
-    } else {
-      if (rho >= gsz * a.n_extra) break;
-      rr = extra_row(a.hg, grp, a.n_extra, rho);
-    }
+    if (rho >= group_rows) break;
+    const RowRef rr = video ? video_row(a.hg, grp, n, g.S, rho) : extra_row(a.hg, grp, a.n_extra, rho);
     int64_t off;
     int row_index;
     if (video) {
@@ -194,7 +206,8 @@ __global__ __launch_bounds__(256) void k_select_bf16(SelectArgs a, TileSched ts)
       zs += j < n ? E[i] : 0.0f;
     }
     zs = wave_sum(zs);
-    const int cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off);
+    __builtin_amdgcn_wave_barrier();  // all lanes have read the row before it is reused
+    const int cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off, &sZ[row * NCAP]);
     if (lane == 0) a.sel_count[(size_t)rr.hq * a.rows_per_head + row_index] = cnt;
   }
 }
@@ -203,6 +216,7 @@ __global__ __launch_bounds__(256) void k_select_bf16(SelectArgs a, TileSched ts)
 // computes its dot products serially in float32.
 template <int D, int NPL>
 __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_video_rows) {
+  __shared__ float scratch[4][kWave];
   const KGeom& g = a.g;
   const int lane = threadIdx.x & (kWave - 1);
   const int row_id = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -257,19 +271,55 @@ __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_vide
     zs += j < n ? E[i] : 0.0f;
   }
   zs = wave_sum(zs);
-  const int cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off);
+  const int cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off, scratch[threadIdx.x / kWave]);
   if (lane == 0) a.sel_count[(size_t)hq * a.rows_per_head + row_index] = cnt;
 }
 
+// One launch serves video query cubes [c_lo, c_hi) and, if with_extra, the
+// extra rows (which have Nc candidates).
 template <int D, int RT, int NPL>
-static void launch_bf16(const SelectArgs& a, hipStream_t s) {
+static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, bool with_extra) {
   TileSched ts;
   const int gmax = a.hg.gmax;
   ts.video_tiles_per_group = a.has_video ? (gmax * a.g.S + RT - 1) / RT : 0;
-  ts.extra_tiles_per_group = a.n_extra ? (gmax * a.n_extra + RT - 1) / RT : 0;
+  ts.extra_tiles_per_group = (with_extra && a.n_extra) ? (gmax * a.n_extra + RT - 1) / RT : 0;
   ts.n_extra_tiles = a.g.Hkv * ts.extra_tiles_per_group;
-  const int blocks = ts.n_extra_tiles + (a.has_video ? a.g.Nc * a.g.Hkv * ts.video_tiles_per_group : 0);
-  hipLaunchKernelGGL((k_select_bf16<D, RT, NPL>), dim3(blocks), dim3(256), 0, s, a, ts);
+  ts.c_lo = c_lo;
+  ts.c_hi = c_hi;
+  const int nc = a.has_video && c_hi > c_lo ? c_hi - c_lo : 0;
+  const int blocks = ts.n_extra_tiles + nc * a.g.Hkv * ts.video_tiles_per_group;
+  if (blocks > 0)
+    hipLaunchKernelGGL((k_select_bf16<D, RT, NPL>), dim3(blocks), dim3(64 * kSelWaves), 0, s, a, ts);
+}
+
+// Video rows of query cube c have c candidates; split them by capacity so
+// that every launch runs loops sized for its candidates (heaviest first).
+template <int D>
+static void launch_bf16_all(const SelectArgs& a, hipStream_t s) {
+  const int Nc = a.g.Nc;
+  const int cap_extra = Nc;  // extra rows' candidate count
+  auto range = [&](int lo, int hi) { return std::make_pair(std::min(lo, Nc), std::min(hi, Nc)); };
+  // [lo, hi) of query cubes handled at each capacity; extra rows go with the
+  // capacity that holds Nc.
+  {
+    auto r = range(1024, 4096);
+    if (r.second > r.first || cap_extra > 1024) launch_bf16<D, 8, 64>(a, s, r.first, r.second, cap_extra > 1024);
+  }
+  {
+    auto r = range(512, 1024);
+    const bool ex = cap_extra > 512 && cap_extra <= 1024;
+    if (r.second > r.first || ex) launch_bf16<D, 32, 16>(a, s, r.first, r.second, ex);
+  }
+  {
+    auto r = range(256, 512);
+    const bool ex = cap_extra > 256 && cap_extra <= 512;
+    if (r.second > r.first || ex) launch_bf16<D, 32, 8>(a, s, r.first, r.second, ex);
+  }
+  {
+    auto r = range(0, 256);
+    const bool ex = cap_extra <= 256;
+    if (r.second > r.first || ex) launch_bf16<D, 32, 4>(a, s, r.first, r.second, ex);
+  }
 }
 
 template <int D, int NPL>
@@ -282,13 +332,8 @@ static void launch_f32(const SelectArgs& a, hipStream_t s) {
 hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s) {
   const int Nc = a.g.Nc;
   if (dt == ADAS_BF16) {
-    if (a.g.D == 128) {
-      if (Nc <= 1024) launch_bf16<128, 16, 16>(a, s);
-      else launch_bf16<128, 4, 64>(a, s);
-    } else {
-      if (Nc <= 1024) launch_bf16<64, 16, 16>(a, s);
-      else launch_bf16<64, 4, 64>(a, s);
-    }
+    if (a.g.D == 128) launch_bf16_all<128>(a, s);
+    else launch_bf16_all<64>(a, s);
   } else {
     if (a.g.D == 128) {
       if (Nc <= 1024) launch_f32<128, 16>(a, s);
@@ -300,5 +345,7 @@ hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+size_t select_workspace_bytes(const KGeom&, adas_dtype) { return 0; }
 
 }  // namespace adas

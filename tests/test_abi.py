@@ -1,0 +1,134 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol declared
+in include/adas.h, sizes buffers by the closed forms, and rejects invalid
+arguments on the host before any launch (no GPU needed; no compute call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+LIB = os.path.join(ROOT, "adaptive_cube_sparse_amd", "libadas.so")
+HEADER = os.path.join(ROOT, "include", "adas.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libadas.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(adas_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(names) == set(L.EXPORTS)
+
+
+def _geom(**kw):
+    import adaptive_cube_sparse_amd._lib as L
+    base = dict(T=8, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=6, n_kv_heads=2, head_dim=128)
+    base.update(kw)
+    g = L._Geom(**base)
+    return g
+
+
+def test_version_and_status_strings():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    assert lib.adas_version().decode() == "0.1"
+    for s in range(8):
+        assert lib.adas_status_string(s).decode().startswith("ADAS_")
+
+
+def test_capacity_and_workspace_closed_forms():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _geom()
+    N, S, Nc, Hq = 8 * 16 * 16, 64, 32, 6
+    capv = S * Nc * (Nc - 1) // 2
+    assert lib.adas_sel_capacity(ctypes.byref(g), 1, 0) == Hq * capv
+    assert lib.adas_sel_capacity(ctypes.byref(g), 1, 5) == Hq * capv + Hq * 5 * Nc
+    assert lib.adas_sel_capacity(ctypes.byref(g), 0, 5) == Hq * 5 * Nc
+    # the selection keeps its logits on chip and needs no workspace
+    assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_SELECT, 1, 0) == 0
+    assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_F32, L.ADAS_WS_SELECT, 1, 0) == 0
+    # prefill without extra rows needs no attention workspace
+    assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_ATTN, 1, 0) == 0
+    bad = _geom(ct=3)
+    assert lib.adas_sel_capacity(ctypes.byref(bad), 1, 0) == -1
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _select(lib, g, **kw):
+    import adaptive_cube_sparse_amd._lib as L
+    args = dict(dtype=L.ADAS_BF16, q_cube=FAKE, n_extra=0, q_extra=None, kbar=FAKE, p=0.7,
+                sel_count=FAKE, sel_idx=FAKE, cap=1 << 40, ws=FAKE, ws_bytes=1 << 40)
+    args.update(kw)
+    return lib.adas_select_topp(ctypes.byref(g) if g is not None else None, args["dtype"],
+                                args["q_cube"], args["n_extra"], args["q_extra"], args["kbar"],
+                                args["p"], args["sel_count"], args["sel_idx"], args["cap"],
+                                args["ws"], args["ws_bytes"], None)
+
+
+def test_select_rejects_invalid_arguments_on_host():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _geom()
+    assert _select(lib, None) == L.ADAS_ERR_NULL
+    for p in (0.0, -0.1, 1.0001, float("nan")):
+        assert _select(lib, g, p=p) == L.ADAS_ERR_VALUE
+    assert "p must be" in lib.adas_last_error().decode()
+    assert _select(lib, _geom(ct=3)) == L.ADAS_ERR_SHAPE
+    assert _select(lib, _geom(head_dim=96)) == L.ADAS_ERR_SHAPE
+    assert _select(lib, _geom(n_q_heads=5)) == L.ADAS_ERR_SHAPE       # Hkv must divide Hq
+    assert _select(lib, g, dtype=7) == L.ADAS_ERR_DTYPE
+    assert _select(lib, g, q_cube=None) == L.ADAS_ERR_SHAPE           # no rows at all
+    assert _select(lib, g, n_extra=3, q_extra=None) == L.ADAS_ERR_NULL
+    assert _select(lib, g, kbar=None) == L.ADAS_ERR_NULL
+    assert _select(lib, g, cap=10) == L.ADAS_ERR_CAPACITY
+    big = _geom(T=8, H=16, W=16 * 9, ct=1, ch=1, cw=4)               # 9216 cubes > 4096
+    assert _select(lib, big) == L.ADAS_ERR_SHAPE
+    # head_map entries must name an existing KV head
+    hm = (ctypes.c_int32 * 6)(0, 1, 0, 1, 2, 0)
+    g2 = _geom()
+    g2.head_map = ctypes.cast(hm, ctypes.POINTER(ctypes.c_int32))
+    assert _select(lib, g2) == L.ADAS_ERR_VALUE
+
+
+def test_attention_and_partition_reject_invalid_arguments_on_host():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _geom()
+    # partition: null buffers, bad head count, bad dtype
+    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 2, None, FAKE, None, None) == L.ADAS_ERR_NULL
+    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 0, FAKE, FAKE, None, None) == L.ADAS_ERR_SHAPE
+    assert lib.adas_cube_partition(ctypes.byref(g), 9, 2, FAKE, FAKE, None, None) == L.ADAS_ERR_DTYPE
+    assert lib.adas_cube_mean_keys(ctypes.byref(g), L.ADAS_BF16, None, FAKE, None) == L.ADAS_ERR_NULL
+
+    def attn(**kw):
+        a = dict(q_cube=FAKE, k=FAKE, v=FAKE, n_extra=0, n_text_kv=0, q_extra=None, kt=None, vt=None,
+                 cnt=FAKE, idx=FAKE, out=FAKE, out_x=None, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.adas_sparse_attn_fwd(ctypes.byref(g), L.ADAS_BF16, a["q_cube"], a["k"], a["v"],
+                                        a["n_extra"], a["n_text_kv"], a["q_extra"], a["kt"], a["vt"],
+                                        a["cnt"], a["idx"], a["out"], a["out_x"], a["ws"],
+                                        a["ws_bytes"], None)
+    assert attn(k=None) == L.ADAS_ERR_NULL
+    assert attn(out=None) == L.ADAS_ERR_NULL
+    assert attn(n_extra=4, q_extra=FAKE, out_x=None) == L.ADAS_ERR_NULL
+    assert attn(n_extra=4, n_text_kv=3, q_extra=FAKE, out_x=FAKE) == L.ADAS_ERR_SHAPE
+    assert attn(n_extra=4, n_text_kv=4, q_extra=FAKE, out_x=FAKE) == L.ADAS_ERR_NULL  # no text K/V
+    assert attn(q_cube=None) == L.ADAS_ERR_SHAPE
+    # decode rows split across cube chunks need a workspace
+    need = lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_ATTN, 0, 2)
+    assert need > 0
+    assert attn(q_cube=None, out=None, n_extra=2, q_extra=FAKE, out_x=FAKE) == L.ADAS_ERR_WORKSPACE
