@@ -25,6 +25,9 @@ COMMON_FLAGS = [
     # keep the compiler from forming packed fp32 ALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # the kernels never see NaN inputs on purpose; without this every fmaxf on an
+    # MFMA result is preceded by a canonicalizing v_max
+    "-fno-honor-nans",
 ]
 
 

@@ -32,6 +32,7 @@ namespace adas {
 typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4u __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2u __attribute__((ext_vector_type(2)));
 
 namespace {
 constexpr int UKB = 64;      // keys per key block
@@ -67,7 +68,9 @@ struct USmem {
   int n_union;
 };
 
-template <int D>
+// FULL: every key block holds UKB valid keys (S a multiple of UKB), so the
+// video phases never need per-key masks.
+template <int D, bool FULL>
 __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using Sm = USmem<D>;
   __shared__ Sm sm;
@@ -146,6 +149,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     }
   }
   const float qscale = kLog2eU / sqrtf((float)D);
+  const bf16x2u kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // running softmax state of the lane's row (identical in both lane halves)
   float m_run = -INFINITY, l_run = 0.f;
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     }
     float mb = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mb = fmaxf(mb, fmaxf(st[0][i], st[1][i]));
+    for (int i = 1; i < 16; ++i) mb = fmaxf(fmaxf(mb, st[0][i]), st[1][i]);  // v_max3
     mb = fmaxf(mb, xor32_f32(mb));
     const float mb_c = rowsel ? mb * qscale : -INFINITY;
     const bool grow = mb_c > m_run + kLazy;
@@ -251,15 +255,20 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       m_run = grow ? mb_c : m_run;
     }
     const float bias = (rowsel && m_run != -INFINITY) ? m_run : INFINITY;
-    float ls = 0.f;
+    // P in bf16; the row sum is taken over the same bf16 values the PV product
+    // uses (two per v_dot2 against (1, 1)), so numerator and denominator agree.
     bf16x8u pb[4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = ex2(fmaf(st[h2][i], qscale, -bias));
-        ls += p;
-        pb[2 * h2 + i / 8][i % 8] = (__bf16)p;
+      for (int i = 0; i < 16; ++i) pb[2 * h2 + i / 8][i % 8] = (__bf16)ex2(fmaf(st[h2][i], qscale, -bias));
+    float ls = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2u pair = {pb[u][2 * e], pb[u][2 * e + 1]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ls, false);
       }
     ls += xor32_f32(ls);
     l_run += ls;
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         },
         [&](int, int buf, int kc) __attribute__((always_inline)) {
           if (!wave_has_rows) return;
-          if (kc == UKB) compute(kFull{}, buf, row_ok, kc, false, 0);
+          if (FULL || kc == UKB) compute(kFull{}, buf, row_ok, kc, false, 0);
           else compute(kMasked{}, buf, row_ok, kc, false, 0);
         });
   }
@@ -435,7 +444,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
           const uint32_t mw = sm.bits[UNW * ul + wave];
           if (mw == 0u) return;
           const bool sel = ((mw >> lr) & 1u) != 0u;
-          if (kc == UKB) compute(kFull{}, buf, sel, kc, false, 0);
+          if (FULL || kc == UKB) compute(kFull{}, buf, sel, kc, false, 0);
           else compute(kMasked{}, buf, sel, kc, false, 0);
         });
   }
@@ -498,8 +507,12 @@ hipError_t launch_union(const AttnArgs& a, hipStream_t s) {
     }
   }
   const long blocks = sc.n_extra_wgs + video_blocks;
-  if (blocks > 0)
-    hipLaunchKernelGGL((k_attn_union<D>), dim3((unsigned)blocks), dim3(UNT), 0, s, a, sc);
+  if (blocks > 0) {
+    if (a.g.S % UKB == 0)
+      hipLaunchKernelGGL((k_attn_union<D, true>), dim3((unsigned)blocks), dim3(UNT), 0, s, a, sc);
+    else
+      hipLaunchKernelGGL((k_attn_union<D, false>), dim3((unsigned)blocks), dim3(UNT), 0, s, a, sc);
+  }
   return hipGetLastError();
 }
 
