@@ -60,7 +60,7 @@ struct USched {
 template <int D>
 struct USmem {
   static constexpr int KS = D + 8;    // bf16 stride of a K row (68 dwords: conflict-free b128 reads)
-  static constexpr int VS = UKB + 4;  // bf16 stride of a V^T row (34 dwords: conflict-free b64 reads)
+  static constexpr int VS = UKB + 8;  // bf16 stride of a V^T row (36 dwords: conflict-free b128 reads)
   uint16_t k[2][UKB * KS];
   uint16_t vt[2][D * VS];
   uint32_t bits[UPASS * UNW];  // [cube in pass][wave] -> rows of the wave that selected it
@@ -163,11 +163,15 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // K: 16-byte vector e = tid + UNT*u -> key e / VPR, chunk e % VPR (row-major copy).
   // V: thread (key pair kp, d-chunk vc) loads keys 2kp, 2kp+1 and writes V^T
   //    rows 8vc..8vc+7 as 32-bit pairs.  The two lane halves of a wave take
-  //    d-chunks two apart, so a 64-lane store covers 64 distinct banks.
+  //    adjacent d-chunks (rows 8 apart = 32 banks apart), so a 64-lane store
+  //    covers 64 distinct banks.  Inside each group of 16 keys, key bits 2 and
+  //    3 are swapped in the V^T column order: the 8 keys one lane feeds to a
+  //    PV k-step are then contiguous, read as one b128.
   constexpr int VPR = D / 8;
   constexpr int NK = UKB * VPR / UNT;  // K vectors per thread (2 for D = 128, 1 for D = 64)
   const int kp = lane & 31;
-  const int vc = 4 * (wave >> 1) + (wave & 1) + 2 * lh;
+  const int vc = 2 * wave + lh;
+  const int vcol = (2 * kp & ~12) | ((2 * kp & 4) << 1) | ((2 * kp & 8) >> 1);  // V^T column of key 2kp
   const bool v_thread = vc < VPR;
   uint4 kr[NK], vr[2];
   auto fetch = [&](const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) __attribute__((always_inline)) {
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       for (int e = 0; e < 8; ++e) {
         const uint32_t lo = (e & 1) ? (w0[e / 2] >> 16) : (w0[e / 2] & 0xFFFFu);
         const uint32_t hi = (e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16);
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][(8 * vc + e) * Sm::VS + 2 * kp]) = lo | hi;
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][(8 * vc + e) * Sm::VS + vcol]) = lo | hi;
       }
     }
   };
@@ -273,16 +277,15 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     ls += xor32_f32(ls);
     l_run += ls;
     // O^T += V^T P^T over 4 k-steps of 16 keys; slot 8*lh + e of k-step u
-    // holds key 16*u + 8*(e/4) + 4*lh + (e%4).
+    // holds key 16*u + 8*(e/4) + 4*lh + (e%4), which V^T keeps in column
+    // 16*u + 8*lh + e.
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (!PKM || 16 * u < kc) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* vrow = &vbuf[(32 * db + lr) * Sm::VS + 16 * u + 4 * lh];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8u va = __builtin_bit_cast(bf16x8u, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const bf16x8u va = __builtin_bit_cast(
+              bf16x8u, *reinterpret_cast<const uint4*>(&vbuf[(32 * db + lr) * Sm::VS + 16 * u + 8 * lh]));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], acc[db], 0, 0, 0);
         }
       }
