@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 from ._lib import (  # noqa: F401
-    ADAS_BF16, ADAS_F32, ADAS_WS_ATTN, ADAS_WS_SELECT, AdasError, Geometry, LIB_PATH,
+    ADAS_BF16, ADAS_F32, ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT, ADAS_WS_ATTN, ADAS_WS_SELECT,
+    AdasError, Geometry, LIB_PATH,
     adas_cube_mean_keys, adas_cube_partition, adas_select_topp, adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
 )
@@ -45,7 +46,8 @@ class AdasAttention:
         dev = torch.device(device)
         e = dict(device=dev, dtype=dtype)
         self.k_cube = torch.empty((g.n_kv_heads, g.N, g.head_dim), **e)
-        self.v_cube = torch.empty((g.n_kv_heads, g.N, g.head_dim), **e)
+        # values are kept cube-transposed (ADAS_LAYOUT_VT), the layout the attention reads
+        self.v_cube = torch.empty((g.n_kv_heads, g.n_cubes, g.head_dim, g.S), **e)
         self.perm = torch.empty((g.N,), device=dev, dtype=torch.int32)
         self.kbar = torch.empty((g.n_kv_heads, g.n_cubes, g.head_dim), device=dev, dtype=torch.float32)
         self.q_cube = torch.empty((g.n_q_heads, g.N, g.head_dim), **e) if has_video else None
@@ -64,10 +66,11 @@ class AdasAttention:
 
     # -- steps ---------------------------------------------------------------
     def build_kv(self, k_raster: torch.Tensor, v_raster: torch.Tensor, stream=None):
-        """Partition K and V into cube layout and compute the cube mean keys."""
+        """Partition K (token rows) and V (cube-transposed) into cube layout and
+        compute the cube mean keys."""
         g = self.geom
         adas_cube_partition(g, k_raster, self.k_cube, self.perm, stream)
-        adas_cube_partition(g, v_raster, self.v_cube, None, stream)
+        adas_cube_partition(g, v_raster, self.v_cube, None, stream, layout=ADAS_LAYOUT_VT)
         adas_cube_mean_keys(g, self.k_cube, self.kbar, stream)
 
     def partition_queries(self, q_raster: torch.Tensor, stream=None):

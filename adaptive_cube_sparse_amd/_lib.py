@@ -21,6 +21,7 @@ ADAS_OK, ADAS_ERR_NULL, ADAS_ERR_SHAPE, ADAS_ERR_VALUE, ADAS_ERR_DTYPE, \
     ADAS_ERR_WORKSPACE, ADAS_ERR_CAPACITY, ADAS_ERR_HIP = range(8)
 ADAS_BF16, ADAS_F32 = 0, 1
 ADAS_WS_SELECT, ADAS_WS_ATTN = 0, 1
+ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT = 0, 1
 ADAS_MAX_HEADS = 128
 ADAS_MAX_CUBES = 4096
 
@@ -58,7 +59,7 @@ def load() -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     gp = ctypes.POINTER(_Geom)
     sig = {
-        "adas_cube_partition": (i32, [gp, i32, i32, vp, vp, vp, vp]),
+        "adas_cube_partition": (i32, [gp, i32, i32, i32, vp, vp, vp, vp]),
         "adas_cube_mean_keys": (i32, [gp, i32, vp, vp, vp]),
         "adas_select_topp": (i32, [gp, i32, vp, i32, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
         "adas_sparse_attn_fwd": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -160,14 +161,20 @@ def _check(status: int, where: str):
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
 def adas_cube_partition(geom: Geometry, x_raster: torch.Tensor, x_cube: torch.Tensor,
-                        perm: Optional[torch.Tensor] = None, stream=None) -> None:
-    """x_raster [N][nh][d] -> x_cube [nh][N][d] (+ perm [N] int32)."""
+                        perm: Optional[torch.Tensor] = None, stream=None,
+                        layout: int = ADAS_LAYOUT_TOKENS) -> None:
+    """x_raster [N][nh][d] -> x_cube [nh][N][d] (ADAS_LAYOUT_TOKENS) or
+    [nh][Nc][d][S] (ADAS_LAYOUT_VT, the value layout of the attention), plus
+    perm [N] int32."""
     lib = load()
     N, nh, d = x_raster.shape
-    _shape(x_cube, (nh, N, d), "x_cube")
+    if layout == ADAS_LAYOUT_VT:
+        _shape(x_cube, (nh, geom.n_cubes, d, geom.S), "x_cube")
+    else:
+        _shape(x_cube, (nh, N, d), "x_cube")
     _shape(perm, (N,), "perm")
     g, keep = geom._c()
-    st = lib.adas_cube_partition(ctypes.byref(g), _dtype_code(x_raster), nh,
+    st = lib.adas_cube_partition(ctypes.byref(g), _dtype_code(x_raster), nh, int(layout),
                                  _ptr(x_raster, name="x_raster"),
                                  _ptr(x_cube, x_raster.dtype, "x_cube"),
                                  _ptr(perm, torch.int32, "perm"), _stream(stream))
@@ -222,7 +229,7 @@ def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text
     Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
     _shape(q_cube, (Hq, geom.N, d), "q_cube")
     _shape(k_cube, (Hkv, geom.N, d), "k_cube")
-    _shape(v_cube, (Hkv, geom.N, d), "v_cube")
+    _shape(v_cube, (Hkv, geom.n_cubes, d, geom.S), "v_cube")  # ADAS_LAYOUT_VT
     _shape(out_raster, (geom.N, Hq, d), "out_raster")
     if n_extra:
         _shape(q_extra, (n_extra, Hq, d), "q_extra")

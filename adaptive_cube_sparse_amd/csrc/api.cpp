@@ -104,19 +104,21 @@ int64_t capacity_of(const adas::KGeom& g, bool has_video, int n_extra) {
 extern "C" {
 
 adas_status adas_cube_partition(const adas_geom* geom, adas_dtype dtype, int32_t n_heads,
-                                const void* x_raster, void* x_cube, int32_t* perm,
-                                void* stream) {
+                                adas_layout layout, const void* x_raster, void* x_cube,
+                                int32_t* perm, void* stream) {
   adas::KGeom g;
   adas::HeadGroups hg;
   adas_status st = derive(geom, g, hg);
   if (st != ADAS_OK) return st;
   if ((st = check_dtype(dtype)) != ADAS_OK) return st;
+  if (layout != ADAS_LAYOUT_TOKENS && layout != ADAS_LAYOUT_VT)
+    return fail(ADAS_ERR_VALUE, "layout must be ADAS_LAYOUT_TOKENS or ADAS_LAYOUT_VT");
   if (x_raster == nullptr || x_cube == nullptr) return fail(ADAS_ERR_NULL, "x_raster/x_cube is NULL");
   if (n_heads <= 0 || n_heads > ADAS_MAX_HEADS)
     return fail(ADAS_ERR_SHAPE, "n_heads must be in [1, %d]", ADAS_MAX_HEADS);
   const int eb = dtype == ADAS_BF16 ? 2 : 4;
-  return hip_status(adas::launch_partition(g, eb, n_heads, x_raster, x_cube, perm,
-                                           (hipStream_t)stream),
+  return hip_status(adas::launch_partition(g, eb, n_heads, layout == ADAS_LAYOUT_VT, x_raster,
+                                           x_cube, perm, (hipStream_t)stream),
                     "adas_cube_partition launch");
 }
 

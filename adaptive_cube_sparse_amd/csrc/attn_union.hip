@@ -8,9 +8,11 @@
 // query operands and float32 output accumulators stay in registers for the
 // whole tile.  The workgroup walks the union of its rows' selected cubes (plus
 // the own cube, or the causal text keys), one key block of 64 keys at a time:
-//   * K and V of a block are staged in LDS (V transposed) in one of two
-//     buffers; block i+1 is fetched into registers and staged while block i is
-//     computed, so each block costs one barrier;
+//   * K rows and V^T rows (values arrive cube-transposed, ADAS_LAYOUT_VT) of a
+//     block are staged in LDS.  When every block is full (S a multiple of 64)
+//     video blocks move global -> LDS with global_load_lds_dwordx4, two blocks
+//     ahead over three buffers; otherwise, and for text keys, through
+//     registers one block ahead.  Either way one barrier per block;
 //   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, applies a
 //     per-row selection bit (row x cube bitmap built from the selection lists)
 //     as a +inf softmax bias, keeps the online softmax in log2 units with lazy
@@ -61,11 +63,6 @@ template <int D>
 struct USmem {
   static constexpr int KS = D + 8;    // bf16 stride of a K row (68 dwords: conflict-free b128 reads)
   static constexpr int VS = UKB + 8;  // bf16 stride of a V^T row (36 dwords: conflict-free b128 reads)
-  uint16_t k[2][UKB * KS];
-  uint16_t vt[2][D * VS];
-  uint32_t bits[UPASS * UNW];  // [cube in pass][wave] -> rows of the wave that selected it
-  uint16_t ulist[UPASS];       // cubes of the pass selected by any row
-  int n_union;
 };
 
 // FULL: every key block holds UKB valid keys (S a multiple of UKB), so the
@@ -73,7 +70,26 @@ struct USmem {
 template <int D, bool FULL>
 __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using Sm = USmem<D>;
-  __shared__ Sm sm;
+  // Three K and three V^T block buffers as separate LDS objects, so that the
+  // compiler can tell reads of one from asynchronous global->LDS loads into
+  // another.
+  __shared__ __attribute__((aligned(16))) uint16_t lk0[UKB * Sm::KS], lk1[UKB * Sm::KS], lk2[UKB * Sm::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t lv0[D * Sm::VS], lv1[D * Sm::VS], lv2[D * Sm::VS];
+  __shared__ uint32_t s_bits[UPASS * UNW];  // [cube in pass][wave] -> rows of the wave that selected it
+  __shared__ uint16_t s_ulist[UPASS];       // cubes of the pass selected by any row
+  __shared__ int s_nunion;
+  auto kbuf_rt = [&](int b) __attribute__((always_inline)) { return b == 0 ? lk0 : (b == 1 ? lk1 : lk2); };
+  auto vbuf_rt = [&](int b) __attribute__((always_inline)) { return b == 0 ? lv0 : (b == 1 ? lv1 : lv2); };
+  auto kbuf_c = [&](auto c) __attribute__((always_inline)) {
+    if constexpr (decltype(c)::value == 0) return lk0;
+    else if constexpr (decltype(c)::value == 1) return lk1;
+    else return lk2;
+  };
+  auto vbuf_c = [&](auto c) __attribute__((always_inline)) {
+    if constexpr (decltype(c)::value == 0) return lv0;
+    else if constexpr (decltype(c)::value == 1) return lv1;
+    else return lv2;
+  };
   const KGeom& g = a.g;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -159,22 +175,30 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  // ---- K/V staging --------------------------------------------------------------------
+  // ---- K/V staging through registers -------------------------------------------------
   // K: 16-byte vector e = tid + UNT*u -> key e / VPR, chunk e % VPR (row-major copy).
-  // V: thread (key pair kp, d-chunk vc) loads keys 2kp, 2kp+1 and writes V^T
-  //    rows 8vc..8vc+7 as 32-bit pairs.  The two lane halves of a wave take
-  //    adjacent d-chunks (rows 8 apart = 32 banks apart), so a 64-lane store
-  //    covers 64 distinct banks.  Inside each group of 16 keys, key bits 2 and
-  //    3 are swapped in the V^T column order: the 8 keys one lane feeds to a
-  //    PV k-step are then contiguous, read as one b128.
+  // V from ADAS_LAYOUT_VT (video cubes): 16-byte piece e = tid + UNT*u -> V^T
+  //    row e / 8, keys 8*(e % 8) .. +8 of the block, already in V^T column
+  //    order; a plain copy.
+  // V from token-major text: thread (key pair kp, d-chunk vc) loads keys 2kp,
+  //    2kp+1 and writes V^T rows 8vc..8vc+7 as 32-bit pairs.  The two lane
+  //    halves of a wave take adjacent d-chunks (rows 8 apart = 32 banks apart),
+  //    so a 64-lane store covers 64 distinct banks.
+  // V^T column order: inside each group of 16 keys, key bits 2 and 3 are
+  // swapped, so the 8 keys one lane feeds to a PV k-step are contiguous and
+  // read as one b128 (the same order ADAS_LAYOUT_VT stores).
   constexpr int VPR = D / 8;
-  constexpr int NK = UKB * VPR / UNT;  // K vectors per thread (2 for D = 128, 1 for D = 64)
+  constexpr int NK = UKB * VPR / UNT;       // K vectors per thread (2 for D = 128, 1 for D = 64)
+  constexpr int NVT = D * (UKB / 8) / UNT;  // V^T pieces per thread (same counts)
+  static_assert(NVT <= 2, "vr holds two vectors");
   const int kp = lane & 31;
   const int vc = 2 * wave + lh;
   const int vcol = (2 * kp & ~12) | ((2 * kp & 4) << 1) | ((2 * kp & 8) >> 1);  // V^T column of key 2kp
   const bool v_thread = vc < VPR;
   uint4 kr[NK], vr[2];
-  auto fetch = [&](const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) __attribute__((always_inline)) {
+  // vt: V comes cube-transposed (row stride vstride = S elements); else
+  // token-major with the K stride.
+  auto fetch = [&](bool vt, const uint16_t* kb, const uint16_t* vb, size_t stride, int kc) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int e = tid + UNT * u;
@@ -182,28 +206,44 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       kr[u] = key < kc ? *reinterpret_cast<const uint4*>(kb + key * stride + ch * 8)
                        : make_uint4(0, 0, 0, 0);
     }
+    if (vt) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = 2 * kp + u;
-      vr[u] = (v_thread && key < kc) ? *reinterpret_cast<const uint4*>(vb + key * stride + vc * 8)
-                                     : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < NVT; ++u) {
+        const int e = tid + UNT * u;
+        const int row = e >> 3, c8 = e & 7;
+        vr[u] = 8 * c8 < kc ? *reinterpret_cast<const uint4*>(vb + (size_t)row * g.S + 8 * c8)
+                            : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = 2 * kp + u;
+        vr[u] = (v_thread && key < kc) ? *reinterpret_cast<const uint4*>(vb + key * stride + vc * 8)
+                                       : make_uint4(0, 0, 0, 0);
+      }
     }
   };
-  auto stage = [&](int buf) __attribute__((always_inline)) {
+  auto stage = [&](bool vt, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int e = tid + UNT * u;
       const int key = e / VPR, ch = e % VPR;
-      *reinterpret_cast<uint4*>(&sm.k[buf][key * Sm::KS + ch * 8]) = kr[u];
+      *reinterpret_cast<uint4*>(&kbuf_rt(buf)[key * Sm::KS + ch * 8]) = kr[u];
     }
-    if (v_thread) {
+    if (vt) {
+#pragma unroll
+      for (int u = 0; u < NVT; ++u) {
+        const int e = tid + UNT * u;
+        *reinterpret_cast<uint4*>(&vbuf_rt(buf)[(e >> 3) * Sm::VS + 8 * (e & 7)]) = vr[u];
+      }
+    } else if (v_thread) {
       const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
       const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t lo = (e & 1) ? (w0[e / 2] >> 16) : (w0[e / 2] & 0xFFFFu);
         const uint32_t hi = (e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16);
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][(8 * vc + e) * Sm::VS + vcol]) = lo | hi;
+        *reinterpret_cast<uint32_t*>(&vbuf_rt(buf)[(8 * vc + e) * Sm::VS + vcol]) = lo | hi;
       }
     }
   };
@@ -211,10 +251,9 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // ---- one key block from buffer `buf`: rowsel = this lane's row takes part --------
   // kc valid keys; causal: key kbase_idx + key must be <= the row's token index.
   // A lane whose row did not select the block gets bias +inf, i.e. P = 0.
-  auto compute = [&](auto per_key_mask, int buf, bool rowsel, int kc, bool causal, int kbase_idx) __attribute__((always_inline)) {
+  auto compute = [&](auto per_key_mask, const uint16_t* kbuf, const uint16_t* vbuf, bool rowsel, int kc, bool causal,
+                     int kbase_idx) __attribute__((always_inline)) {
     constexpr bool PKM = decltype(per_key_mask)::value;
-    const uint16_t* kbuf = sm.k[buf];
-    const uint16_t* vbuf = sm.vt[buf];
     f32x16 st[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -294,28 +333,28 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using kFull = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
 
-  // Pipelined walk over nb key blocks: source(i, kptr, vptr, stride, kc) names
-  // block i, work(i, buf, kc) computes it.  One barrier per block: staging
-  // into buffer i&1 is safe because every wave finished block i-2 before the
-  // barrier of block i-1.
-  auto pipeline = [&](int nb, auto source, auto work) __attribute__((always_inline)) {
+  // Register-staged walk over nb key blocks: source(i, kptr, vptr, stride, kc)
+  // names block i (vt: values cube-transposed), work(i, buf, kc) computes it.
+  // One barrier per block: staging into buffer i&1 is safe because every
+  // wave finished block i-2 before the barrier of block i-1.
+  auto pipeline = [&](bool vt, int nb, auto source, auto work) __attribute__((always_inline)) {
     if (nb <= 0) return;
     __syncthreads();  // the previous phase no longer reads either buffer
     const uint16_t *kp0, *vp0;
     size_t st0;
     int kc0;
     source(0, kp0, vp0, st0, kc0);
-    fetch(kp0, vp0, st0, kc0);
+    fetch(vt, kp0, vp0, st0, kc0);
     int kc_cur = kc0;
     for (int i = 0; i < nb; ++i) {
       const int buf = i & 1;
-      stage(buf);
+      stage(vt, buf);
       int kc_next = 0;
       if (i + 1 < nb) {
         const uint16_t *kpn, *vpn;
         size_t stn;
         source(i + 1, kpn, vpn, stn, kc_next);
-        fetch(kpn, vpn, stn, kc_next);
+        fetch(vt, kpn, vpn, stn, kc_next);
       }
       __syncthreads();
       work(i, buf, kc_cur);
@@ -323,33 +362,136 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     }
   };
 
+  // ---- direct global->LDS staging of video blocks (FULL only) -----------------------
+  // K rows (D*2 bytes) and V^T rows (UKB*2 bytes) land in LDS padded by 16 bytes;
+  // each load instruction moves 64 pieces of 16 bytes to 64 consecutive LDS
+  // slots, so the piece index e = 64*q + lane names (row, column) = divmod(e,
+  // pieces per row); the padding column re-reads the row's first piece.
+  constexpr int KPR = D / 8 + 1;             // pieces per padded K row
+  constexpr int VPRp = UKB / 8 + 1;          // pieces per padded V^T row
+  constexpr int NKI = UKB * KPR / 64;        // K instructions per block
+  constexpr int NVI = D * VPRp / 64;         // V^T instructions per block
+  constexpr int NLI = NKI + NVI;
+  constexpr int NLW = (NLI + UNW - 1) / UNW; // instructions per wave (max)
+  constexpr int NLMIN = NLI / UNW;           // instructions per wave (min)
+  static_assert(UKB * KPR % 64 == 0 && D * VPRp % 64 == 0, "piece counts");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
+  uint32_t dsrc[NLW];
+  uint32_t dlds[NLW];
+  bool disk[NLW], dok[NLW];
+#pragma unroll
+  for (int m = 0; m < NLW; ++m) {
+    const int t = wv + UNW * m;
+    dok[m] = t < NLI;
+    disk[m] = t < NKI;
+    const int q = disk[m] ? t : t - NKI;
+    const int e = 64 * q + lane;
+    if (disk[m]) {
+      const int row = e / KPR, col = e % KPR;
+      dsrc[m] = row * D * 2 + (col == KPR - 1 ? 0 : col * 16);
+      dlds[m] = q * 1024;
+    } else {
+      const int row = e / VPRp, col = e % VPRp;
+      dsrc[m] = row * g.S * 2 + (col == VPRp - 1 ? 0 : col * 16);
+      dlds[m] = q * 1024;
+    }
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  // issue this wave's loads of the block whose K rows start at kb and whose
+  // V^T rows start at vb (bytes), into buffer buf
+  auto issue = [&](const char* kb, const char* vb, auto bufc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NLW; ++m) {
+      if (dok[m]) {
+        if (disk[m])
+          __builtin_amdgcn_global_load_lds((const void*)(kb + dsrc[m]),
+                                           (lds_void*)((char*)kbuf_c(bufc) + dlds[m]), 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds((const void*)(vb + dsrc[m]),
+                                           (lds_void*)((char*)vbuf_c(bufc) + dlds[m]), 16, 0, 0);
+      }
+    }
+  };
+  // Three buffers, loads two blocks ahead, one barrier per block.  Block i+2
+  // goes to buffer (i+2)%3, last read by block i-1, which every wave finished
+  // before the barrier of block i.
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  auto dpipeline = [&](int nb, auto bsrc, auto work) __attribute__((always_inline)) {
+    if (nb <= 0) return;
+    __syncthreads();  // the previous phase no longer reads any buffer
+    {
+      const char *kb, *vb;
+      bsrc(0, kb, vb);
+      issue(kb, vb, C0{});
+      if (nb > 1) { bsrc(1, kb, vb); issue(kb, vb, C1{}); }
+    }
+    // block i sits in buffer i % 3; the loop is unrolled by three so every
+    // buffer is named at compile time
+    auto step = [&](auto bufc, int i) __attribute__((always_inline)) {
+      constexpr int X = decltype(bufc)::value;
+      using Next = std::integral_constant<int, (X + 2) % 3>;
+      if (i + 1 < nb) __builtin_amdgcn_s_waitcnt(0x0F70 | NLMIN);  // vmcnt(NLMIN): block i landed
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (i + 2 < nb) {
+        const char *kb, *vb;
+        bsrc(i + 2, kb, vb);
+        issue(kb, vb, Next{});
+      }
+      work(i, kbuf_c(bufc), vbuf_c(bufc), UKB);
+    };
+    for (int i = 0; i < nb; i += 3) {
+      step(C0{}, i);
+      if (i + 1 >= nb) break;
+      step(C1{}, i + 1);
+      if (i + 2 >= nb) break;
+      step(C2{}, i + 2);
+    }
+  };
+
   const int nkb_cube = (g.S + UKB - 1) / UKB;
   const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.N * D;
-  const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.N * D;
+  const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.N * D;  // [Nc][D][S] (ADAS_LAYOUT_VT)
 
   // ---- own cube (video): every row ------------------------------------------------------
+  const char* vtg = (const char*)a.v_cube + (size_t)grp * g.N * D * 2;  // [Nc][D][S] per group
   if (video) {
+    if constexpr (FULL) {
+      dpipeline(
+          nkb_cube,
+          [&](int i, const char*& kb, const char*& vb) __attribute__((always_inline)) {
+            kb = (const char*)(kg + ((size_t)c * g.S + i * UKB) * D);
+            vb = vtg + (size_t)c * g.S * D * 2 + i * UKB * 2;
+          },
+          [&](int, const uint16_t* kb_, const uint16_t* vb_, int kc) __attribute__((always_inline)) {
+            if (!wave_has_rows) return;
+            compute(kFull{}, kb_, vb_, row_ok, kc, false, 0);
+          });
+    } else {
     pipeline(
-        nkb_cube,
+        true, nkb_cube,
         [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
           const size_t off = ((size_t)c * g.S + i * UKB) * D;
           kp_ = kg + off;
-          vp_ = vg + off;
+          vp_ = vg + (size_t)c * g.S * D + i * UKB;
           st_ = D;
           kc_ = min(UKB, g.S - i * UKB);
         },
         [&](int, int buf, int kc) __attribute__((always_inline)) {
           if (!wave_has_rows) return;
-          if (FULL || kc == UKB) compute(kFull{}, buf, row_ok, kc, false, 0);
-          else compute(kMasked{}, buf, row_ok, kc, false, 0);
+          if (FULL || kc == UKB) compute(kFull{}, kbuf_rt(buf), vbuf_rt(buf), row_ok, kc, false, 0);
+          else compute(kMasked{}, kbuf_rt(buf), vbuf_rt(buf), row_ok, kc, false, 0);
         });
+    }
   }
   // ---- causal text keys (extra rows of a text prefill), chunk 0 --------------------------
   if (!video && a.n_text_kv > 0 && chunk == 0) {
     const uint16_t* kt = (const uint16_t*)a.k_text + (size_t)grp * D;
     const uint16_t* vt = (const uint16_t*)a.v_text + (size_t)grp * D;
     pipeline(
-        (a.n_text_kv + UKB - 1) / UKB,
+        false, (a.n_text_kv + UKB - 1) / UKB,
         [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
           kp_ = kt + (size_t)i * UKB * g.Hkv * D;
           vp_ = vt + (size_t)i * UKB * g.Hkv * D;
@@ -358,7 +500,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         },
         [&](int i, int buf, int kc) __attribute__((always_inline)) {
           const bool sel = row_ok && pos >= i * UKB;
-          if (__ballot(sel) != 0ull) compute(kMasked{}, buf, sel, kc, true, i * UKB);
+          if (__ballot(sel) != 0ull) compute(kMasked{}, kbuf_rt(buf), vbuf_rt(buf), sel, kc, true, i * UKB);
         });
   }
 
@@ -399,7 +541,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     const int je = min(cube_hi, jb + UPASS);
     const int span = je - jb;
     __syncthreads();  // previous users of bits/ulist are done
-    for (int e = tid; e < span * UNW; e += UNT) sm.bits[e] = 0u;
+    for (int e = tid; e < span * UNW; e += UNT) s_bits[e] = 0u;
     __syncthreads();
     if (my_row < n_rows) {
       // entries in [jb, je): binary search for both ends (lists are ascending)
@@ -408,7 +550,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       int lo2 = lo, hi2 = my_cnt;
       while (lo2 < hi2) { const int mid = (lo2 + hi2) >> 1; if (my_list[mid] < je) lo2 = mid + 1; else hi2 = mid; }
       const uint32_t bit = 1u << (my_row & 31);
-      uint32_t* wbase = &sm.bits[my_row >> 5];
+      uint32_t* wbase = &s_bits[my_row >> 5];
 #pragma unroll 4
       for (int i = lo + my_half; i < lo2; i += 2) atomicOr(wbase + UNW * (my_list[i] - jb), bit);
     }
@@ -421,35 +563,53 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         if (u < span) {
           uint32_t o = 0;
 #pragma unroll
-          for (int w = 0; w < UNW; ++w) o |= sm.bits[UNW * u + w];
+          for (int w = 0; w < UNW; ++w) o |= s_bits[UNW * u + w];
           any = o != 0u;
         }
         const uint64_t bal = __ballot(any);
-        if (any) sm.ulist[base + lanes_below(bal)] = (uint16_t)u;
+        if (any) s_ulist[base + lanes_below(bal)] = (uint16_t)u;
         base += popc64(bal);
       }
-      if (lane == 0) sm.n_union = base;
+      if (lane == 0) s_nunion = base;
     }
     __syncthreads();
+    if constexpr (FULL) {
+      dpipeline(
+          s_nunion * nkb_cube,
+          [&](int i, const char*& kb, const char*& vb) __attribute__((always_inline)) {
+            const int ci = i / nkb_cube, kbi = i - ci * nkb_cube;
+            const int j = __builtin_amdgcn_readfirstlane(jb + s_ulist[ci]);
+            kb = (const char*)(kg + ((size_t)j * g.S + kbi * UKB) * D);
+            vb = vtg + (size_t)j * g.S * D * 2 + kbi * UKB * 2;
+          },
+          [&](int i, const uint16_t* kb_, const uint16_t* vb_, int kc) __attribute__((always_inline)) {
+            const int ul = s_ulist[i / nkb_cube];
+            const uint32_t mw = s_bits[UNW * ul + wave];
+            if (mw == 0u) return;
+            const bool sel = ((mw >> lr) & 1u) != 0u;
+            compute(kFull{}, kb_, vb_, sel, kc, false, 0);
+          });
+    } else {
     pipeline(
-        sm.n_union * nkb_cube,
+        true, s_nunion * nkb_cube,
         [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
           const int ci = i / nkb_cube, kb = i - ci * nkb_cube;
-          const int j = jb + sm.ulist[ci];
+          const int j = jb + s_ulist[ci];
           const size_t off = ((size_t)j * g.S + kb * UKB) * D;
           kp_ = kg + off;
-          vp_ = vg + off;
+          vp_ = vg + (size_t)j * g.S * D + kb * UKB;
           st_ = D;
           kc_ = min(UKB, g.S - kb * UKB);
         },
         [&](int i, int buf, int kc) __attribute__((always_inline)) {
-          const int ul = sm.ulist[i / nkb_cube];
-          const uint32_t mw = sm.bits[UNW * ul + wave];
+          const int ul = s_ulist[i / nkb_cube];
+          const uint32_t mw = s_bits[UNW * ul + wave];
           if (mw == 0u) return;
           const bool sel = ((mw >> lr) & 1u) != 0u;
-          if (FULL || kc == UKB) compute(kFull{}, buf, sel, kc, false, 0);
-          else compute(kMasked{}, buf, sel, kc, false, 0);
+          if (FULL || kc == UKB) compute(kFull{}, kbuf_rt(buf), vbuf_rt(buf), sel, kc, false, 0);
+          else compute(kMasked{}, kbuf_rt(buf), vbuf_rt(buf), sel, kc, false, 0);
         });
+    }
   }
 
   // ---- epilogue ----------------------------------------------------------------------

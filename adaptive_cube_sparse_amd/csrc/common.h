@@ -253,11 +253,18 @@ __device__ int topp_select_row(const float (&E)[NPL], int n, float Z, float p,
   return base;
 }
 
+// Column of cube offset r in a value row of ADAS_LAYOUT_VT: bits 2 and 3 of r
+// swapped inside every complete aligned group of 16 offsets, identity in a
+// trailing partial group.  An involution.
+__host__ __device__ inline int vt_column(int r, int S) {
+  return r < (S & ~15) ? ((r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)) : r;
+}
+
 // ---------------------------------------------------------------------------
 // host-side launch entry points (defined in the .hip files)
 // ---------------------------------------------------------------------------
-hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, const void* src, void* dst,
-                            int32_t* perm, hipStream_t s);
+hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, bool vt, const void* src,
+                            void* dst, int32_t* perm, hipStream_t s);
 hipError_t launch_mean_keys(const KGeom& g, adas_dtype dt, const void* k, float* kbar,
                             hipStream_t s);
 

@@ -37,10 +37,59 @@ __global__ __launch_bounds__(256) void k_partition(const uint4* __restrict__ src
   }
 }
 
-hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, const void* src, void* dst,
-                            int32_t* perm, hipStream_t s) {
-  const int vpr = g.D * elem_bytes / 16;
+// ADAS_LAYOUT_VT: one workgroup per (cube, head) stages up to 64 offsets x d
+// in LDS (rows padded by one 32-bit word against bank conflicts), then writes
+// each d-row of the transposed cube: position p of row e takes offset
+// vt_column(p), so consecutive threads write consecutive positions.
+template <typename T>
+__global__ __launch_bounds__(256) void k_partition_vt(const T* __restrict__ src, T* __restrict__ dst,
+                                                      int32_t* __restrict__ perm, KGeom g, int nh) {
+  constexpr int PAD = 4 / (int)sizeof(T);
+  __shared__ T tile[64 * (128 + PAD)];
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int bx = c % g.nW;
+  const int by = (c / g.nW) % g.nH;
+  const int bt = c / (g.nW * g.nH);
+  const int hw = g.ch * g.cw;
+  const int D = g.D, TS = g.D + PAD;
+  T* out = dst + ((size_t)h * g.Nc + c) * (size_t)D * g.S;
+  for (int r0 = 0; r0 < g.S; r0 += 64) {
+    const int nk = min(64, g.S - r0);
+    __syncthreads();  // the previous chunk's reads of `tile` are done
+    for (int e = threadIdx.x; e < nk * D; e += blockDim.x) {
+      const int rr = e / D, col = e - rr * D;
+      const int r = r0 + rr;
+      const int dt = r / hw;
+      const int rem = r - dt * hw;
+      const int dy = rem / g.cw;
+      const int dx = rem - dy * g.cw;
+      const int n = ((bt * g.ct + dt) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
+      tile[rr * TS + col] = src[((size_t)n * nh + h) * D + col];
+      if (perm != nullptr && h == 0 && col == 0) perm[c * g.S + r] = n;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nk * D; e += blockDim.x) {
+      const int d = e / nk, pl = e - d * nk;
+      const int rr = vt_column(r0 + pl, g.S) - r0;  // groups of 16 never straddle r0
+      out[(size_t)d * g.S + r0 + pl] = tile[rr * TS + d];
+    }
+  }
+}
+
+hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, bool vt, const void* src,
+                            void* dst, int32_t* perm, hipStream_t s) {
   dim3 grid(g.Nc, nh);
+  if (vt) {
+    if (elem_bytes == 2)
+      hipLaunchKernelGGL((k_partition_vt<uint16_t>), grid, dim3(256), 0, s, (const uint16_t*)src,
+                         (uint16_t*)dst, perm, g, nh);
+    else
+      hipLaunchKernelGGL((k_partition_vt<uint32_t>), grid, dim3(256), 0, s, (const uint32_t*)src,
+                         (uint32_t*)dst, perm, g, nh);
+    return hipGetLastError();
+  }
+  const int vpr = g.D * elem_bytes / 16;
   hipLaunchKernelGGL(k_partition, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, g,
                      nh, vpr);
   return hipGetLastError();

@@ -58,7 +58,7 @@ typedef enum {
   ADAS_OK = 0,
   ADAS_ERR_NULL = 1,       /* a required pointer is NULL                      */
   ADAS_ERR_SHAPE = 2,      /* grid/cube/head/size arguments are inconsistent  */
-  ADAS_ERR_VALUE = 3,      /* p outside (0, 1], head_map entry out of range   */
+  ADAS_ERR_VALUE = 3,      /* p outside (0, 1], head_map entry or layout bad  */
   ADAS_ERR_DTYPE = 4,      /* unknown dtype                                   */
   ADAS_ERR_WORKSPACE = 5,  /* ws_bytes smaller than adas_workspace_bytes()    */
   ADAS_ERR_CAPACITY = 6,   /* sel_cap smaller than adas_sel_capacity()        */
@@ -80,24 +80,36 @@ typedef struct {
 /* Which call a workspace is sized for. */
 typedef enum { ADAS_WS_SELECT = 0, ADAS_WS_ATTN = 1 } adas_ws_kind;
 
+/* Storage of a cube-layout tensor (see adas_cube_partition). */
+typedef enum { ADAS_LAYOUT_TOKENS = 0, ADAS_LAYOUT_VT = 1 } adas_layout;
+
 /*
  * adas_cube_partition -- cube partition (papernotes.org, key design 1).
  * Copies a token-major tensor into the cube-contiguous, head-major layout
  * used by every other call.  Bit-exact copy.
  *   x_raster [N][n_heads][d]  input, raster token order (as a QKV projection
  *                             emits it)
- *   x_cube   [n_heads][N][d]  output; x_cube[h][c*S + r] = x_raster[n][h]
+ *   layout   ADAS_LAYOUT_TOKENS: x_cube [n_heads][N][d] with
+ *                             x_cube[h][c*S + r] = x_raster[n][h]
+ *            ADAS_LAYOUT_VT:  x_cube [n_heads][Nc][d][S], each cube stored
+ *                             transposed: x_cube[h][c][e][pi(r)] =
+ *                             x_raster[n][h][e], where pi swaps bits 2 and 3
+ *                             of r inside every complete aligned group of 16
+ *                             offsets (pi(r) = r in a trailing partial group).
+ *                             This is the value layout adas_sparse_attn_fwd
+ *                             reads.
  *   perm     [N] int32        optional output (may be NULL): perm[c*S+r] = n
- * Call once for Q (n_heads = Hq) and once each for K and V (n_heads = Hkv).
- * Errors: NULL (x_raster/x_cube), SHAPE, DTYPE, HIP.
+ * Call once for Q and K (n_heads = Hq, Hkv; ADAS_LAYOUT_TOKENS) and once for
+ * V (n_heads = Hkv; ADAS_LAYOUT_VT).
+ * Errors: NULL (x_raster/x_cube), SHAPE, VALUE (unknown layout), DTYPE, HIP.
  */
 adas_status adas_cube_partition(const adas_geom* geom, adas_dtype dtype, int32_t n_heads,
-                                const void* x_raster, void* x_cube, int32_t* perm,
-                                void* stream);
+                                adas_layout layout, const void* x_raster, void* x_cube,
+                                int32_t* perm, void* stream);
 
 /*
  * adas_cube_mean_keys -- cube mean keys kbar_j (papernotes.org, key design 2).
- *   k_cube [Hkv][N][d]   keys in cube layout
+ *   k_cube [Hkv][N][d]   keys in cube layout (ADAS_LAYOUT_TOKENS)
  *   kbar   [Hkv][Nc][d]  float32 output: (1/S) * sum of cube j's S keys,
  *                        accumulated in float64, rounded once to float32
  *                        (round to nearest even).
@@ -151,8 +163,9 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
  *                         its own cube;
  *   extra row (hq, m):    tokens of its selected cubes, plus text tokens
  *                         0..m when n_text_kv > 0 (causal text).
- *   q_cube, k_cube, v_cube  [Hq|Hkv][N][d] cube layout (q_cube NULL: no video
- *                           rows, e.g. decode)
+ *   q_cube, k_cube          [Hq|Hkv][N][d], ADAS_LAYOUT_TOKENS (q_cube NULL: no
+ *                           video rows, e.g. decode)
+ *   v_cube                  [Hkv][Nc][d][S], ADAS_LAYOUT_VT
  *   n_extra, q_extra        as in adas_select_topp
  *   n_text_kv               0 (decode: no text keys) or n_extra (text prefill)
  *   k_text, v_text          [n_extra][Hkv][d] when n_text_kv > 0, else NULL

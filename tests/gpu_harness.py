@@ -97,11 +97,29 @@ class Reference:
         return self.wl.n_q_heads * self.capv + (hq * self.n_extra + m) * self.g.n_cubes
 
 
+def vt_columns(S: int) -> np.ndarray:
+    """Column of each cube offset in ADAS_LAYOUT_VT (include/adas.h): bits 2
+    and 3 swapped inside complete aligned groups of 16, identity in a trailing
+    partial group."""
+    r = np.arange(S)
+    sw = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
+    return np.where(r < (S & ~15), sw, r)
+
+
+def to_vt(x_cube: np.ndarray, S: int) -> np.ndarray:
+    """[nh][N][d] token-row cube layout -> [nh][Nc][d][S] ADAS_LAYOUT_VT."""
+    nh, N, d = x_cube.shape
+    t = x_cube.reshape(nh, N // S, S, d).transpose(0, 1, 3, 2)
+    out = np.empty_like(t)
+    out[..., vt_columns(S)] = t
+    return out
+
+
 def check_layout(ref: Reference, layer):
     """Partition, perm and mean keys: bit-exact."""
     assert np.array_equal(layer.perm.cpu().numpy(), ref.perm), "perm differs"
     assert np.array_equal(bits(layer.k_cube), ref.k_cube), "k_cube differs"
-    assert np.array_equal(bits(layer.v_cube), ref.v_cube), "v_cube differs"
+    assert np.array_equal(bits(layer.v_cube), to_vt(ref.v_cube, ref.g.S)), "v_cube (VT layout) differs"
     if ref.q_cube is not None:
         assert np.array_equal(bits(layer.q_cube), ref.q_cube), "q_cube differs"
     kb = layer.kbar.cpu().numpy()

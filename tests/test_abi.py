@@ -109,9 +109,13 @@ def test_attention_and_partition_reject_invalid_arguments_on_host():
     lib = L.load()
     g = _geom()
     # partition: null buffers, bad head count, bad dtype
-    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 2, None, FAKE, None, None) == L.ADAS_ERR_NULL
-    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 0, FAKE, FAKE, None, None) == L.ADAS_ERR_SHAPE
-    assert lib.adas_cube_partition(ctypes.byref(g), 9, 2, FAKE, FAKE, None, None) == L.ADAS_ERR_DTYPE
+    T, VT = L.ADAS_LAYOUT_TOKENS, L.ADAS_LAYOUT_VT
+    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 2, T, None, FAKE, None, None) == L.ADAS_ERR_NULL
+    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 2, VT, FAKE, None, None, None) == L.ADAS_ERR_NULL
+    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 0, T, FAKE, FAKE, None, None) == L.ADAS_ERR_SHAPE
+    assert lib.adas_cube_partition(ctypes.byref(g), 9, 2, T, FAKE, FAKE, None, None) == L.ADAS_ERR_DTYPE
+    assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 2, 5, FAKE, FAKE, None, None) == L.ADAS_ERR_VALUE
+    assert "layout" in lib.adas_last_error().decode()
     assert lib.adas_cube_mean_keys(ctypes.byref(g), L.ADAS_BF16, None, FAKE, None) == L.ADAS_ERR_NULL
 
     def attn(**kw):
