@@ -185,6 +185,8 @@ static adas_status build_attn(const adas_geom* geom, adas_dtype dtype, const voi
   if (n_text_kv != 0 && n_text_kv != n_extra)
     return fail(ADAS_ERR_SHAPE, "n_text_kv must be 0 or n_extra (%d), got %d", n_extra, n_text_kv);
   if (q_cube == nullptr && n_extra == 0) return fail(ADAS_ERR_SHAPE, "no query rows");
+  if (a.g.Nc > ADAS_MAX_CUBES)  // selection lists exist only up to this many cubes
+    return fail(ADAS_ERR_SHAPE, "%d cubes exceed the limit %d", a.g.Nc, ADAS_MAX_CUBES);
   a.has_video = q_cube != nullptr;
   a.n_extra = n_extra;
   a.n_text_kv = n_text_kv;
@@ -223,7 +225,7 @@ adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const 
   a.sel_idx = sel_idx;
   a.out_raster = out_raster;
   a.out_extra = out_extra;
-  a.partials = (float*)ws;
+  adas::bind_attention_workspace(a, dtype, ws);
   return hip_status(adas::launch_attention(a, dtype, (hipStream_t)stream),
                     "adas_sparse_attn_fwd launch");
 }

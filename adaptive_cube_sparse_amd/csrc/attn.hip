@@ -53,6 +53,28 @@ __global__ __launch_bounds__(256) void k_merge_bf16(AttnArgs a, int n_tiles) {
   for (int i = 0; i < PER; ++i) dst[i] = f32_to_bf16_bits(o[i] / L);
 }
 
+// Selection bitmap of the extra rows: one workgroup per row (hq, m) turns the
+// row's ascending cube list into Nc bits (bit j%32 of word j/32), built with
+// LDS atomics and written out once.  The union kernel reads one word per 32
+// cubes instead of searching the list.
+__global__ __launch_bounds__(256) void k_extra_bitmap(AttnArgs a) {
+  __shared__ uint32_t words[ADAS_MAX_CUBES / 32];
+  const int row = blockIdx.x;  // hq * n_extra + m
+  const int hq = row / a.n_extra, m = row - hq * a.n_extra;
+  const int W = a.bits_words;
+  for (int w = threadIdx.x; w < W; w += blockDim.x) words[w] = 0u;
+  __syncthreads();
+  const int cnt = a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? a.g.N : 0) + m];
+  const int32_t* list = a.sel_idx + extra_list_offset(a.capv, a.g.Hq, a.n_extra, a.g.Nc, hq, m);
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const int j = list[i];
+    atomicOr(&words[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  uint32_t* dst = a.extra_bits + (size_t)row * W;
+  for (int w = threadIdx.x; w < W; w += blockDim.x) dst[w] = words[w];
+}
+
 // ---------------------------------------------------------------------------
 // f32 path: one wave per row.  Keys are processed 64 at a time (one per lane);
 // each lane owns D/64 output dims.
@@ -147,35 +169,62 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_video_ro
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Extra rows (text, decode) are few, so when video tiles do not fill the GPU
+// the cube range of each extra tile is split into chunks of a multiple of 32
+// cubes, aiming at about two workgroups per CU; each chunk writes partial
+// (max, sum, output) rows that k_merge_bf16 combines.
 void plan_attention(AttnArgs& a, adas_dtype dt) {
   a.extra_tiles_per_group = 0;
   a.extra_chunks = 1;
   a.extra_chunk_cubes = a.g.Nc;
+  a.bits_words = (a.g.Nc + 31) / 32;
   if (dt != ADAS_BF16 || a.n_extra == 0) return;
   const int TR = union_tile_rows();
   a.extra_tiles_per_group = (a.hg.gmax * a.n_extra + TR - 1) / TR;
   const int extra_tiles = a.g.Hkv * a.extra_tiles_per_group;
   const long video_wgs = a.has_video
       ? (long)a.g.Nc * a.g.Hkv * ((a.hg.gmax * a.g.S + TR - 1) / TR) : 0;
-  int chunks = 1;
   if (video_wgs < 1024) {
-    const int want = (2048 + extra_tiles - 1) / extra_tiles;
-    const int max_chunks = (a.g.Nc + 7) / 8;  // at least 8 cubes per chunk
-    chunks = want < max_chunks ? want : max_chunks;
-    if (chunks < 1) chunks = 1;
+    const int want = (512 + extra_tiles - 1) / extra_tiles;
+    int cubes = (a.g.Nc + want - 1) / want;
+    cubes = ((cubes + 31) / 32) * 32;
+    if (cubes < 32) cubes = 32;
+    a.extra_chunk_cubes = cubes < a.g.Nc ? cubes : a.g.Nc;
   }
-  a.extra_chunk_cubes = (a.g.Nc + chunks - 1) / chunks;
   a.extra_chunks = (a.g.Nc + a.extra_chunk_cubes - 1) / a.extra_chunk_cubes;
 }
 
+// Workspace of the bf16 attention: [extra-row bitmap][partials], each part
+// 256-byte aligned.
+static size_t bitmap_bytes(const AttnArgs& a) {
+  return ((size_t)a.g.Hq * a.n_extra * a.bits_words * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
 size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt) {
-  if (dt != ADAS_BF16 || a.n_extra == 0 || a.extra_chunks <= 1) return 0;
-  const int TR = union_tile_rows();
-  return (size_t)a.g.Hkv * a.extra_tiles_per_group * a.extra_chunks * TR * (a.g.D + 2) * sizeof(float);
+  if (dt != ADAS_BF16 || a.n_extra == 0) return 0;
+  size_t bytes = bitmap_bytes(a);
+  if (a.extra_chunks > 1) {
+    const int TR = union_tile_rows();
+    bytes += (size_t)a.g.Hkv * a.extra_tiles_per_group * a.extra_chunks * TR * (a.g.D + 2) * sizeof(float);
+  }
+  return bytes;
+}
+
+void bind_attention_workspace(AttnArgs& a, adas_dtype dt, void* ws) {
+  a.extra_bits = nullptr;
+  a.partials = nullptr;
+  if (dt != ADAS_BF16 || a.n_extra == 0) return;
+  a.extra_bits = (uint32_t*)ws;
+  if (a.extra_chunks > 1) a.partials = (float*)((char*)ws + bitmap_bytes(a));
 }
 
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s) {
   if (dt == ADAS_BF16) {
+    if (a.n_extra > 0) {
+      hipLaunchKernelGGL(k_extra_bitmap, dim3((unsigned)(a.g.Hq * a.n_extra)), dim3(256), 0, s, a);
+      const hipError_t eb = hipGetLastError();
+      if (eb != hipSuccess) return eb;
+    }
     hipError_t e = a.g.D == 128 ? launch_union<128>(a, s) : launch_union<64>(a, s);
     if (e != hipSuccess) return e;
     if (a.n_extra > 0 && a.extra_chunks > 1) {

@@ -505,29 +505,17 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   }
 
   // ---- selected cubes -----------------------------------------------------------------
-  // two threads per row walk the row's ascending list
+  // video rows: two threads per row walk the row's ascending list
   const int my_row = tid >> 1, my_half = tid & 1;
   const int32_t* my_list = nullptr;
   int my_cnt = 0;
-  if (my_row < n_rows) {
+  if (video && my_row < n_rows) {
     const int rho = rho0 + my_row;
-    int64_t off;
-    int hq2, row_index;
-    if (video) {
-      const int slot = rho / g.S;
-      hq2 = a.hg.heads[hstart + slot];
-      const int r = rho - slot * g.S;
-      off = video_list_offset(a.capv, hq2, g.S, c, r);
-      row_index = c * g.S + r;
-    } else {
-      const int slot = rho / a.n_extra;
-      hq2 = a.hg.heads[hstart + slot];
-      const int m = rho - slot * a.n_extra;
-      off = extra_list_offset(a.capv, g.Hq, a.n_extra, g.Nc, hq2, m);
-      row_index = (a.has_video ? g.N : 0) + m;
-    }
-    my_list = a.sel_idx + off;
-    my_cnt = a.sel_count[(size_t)hq2 * a.rows_per_head + row_index];
+    const int slot = rho / g.S;
+    const int hq2 = a.hg.heads[hstart + slot];
+    const int r = rho - slot * g.S;
+    my_list = a.sel_idx + video_list_offset(a.capv, hq2, g.S, c, r);
+    my_cnt = a.sel_count[(size_t)hq2 * a.rows_per_head + c * g.S + r];
   }
   int cube_lo, cube_hi;
   if (video) {
@@ -541,9 +529,24 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     const int je = min(cube_hi, jb + UPASS);
     const int span = je - jb;
     __syncthreads();  // previous users of bits/ulist are done
-    for (int e = tid; e < span * UNW; e += UNT) s_bits[e] = 0u;
+    if (!video) {
+      // extra rows: the selection bitmap (one word per 32 cubes, built before
+      // this kernel) gives each (wave, cube) mask as one ballot over the
+      // wave's 32 rows (lanes 0..31)
+      const uint32_t* rbits = a.extra_bits + (size_t)(hq * a.n_extra + pos) * a.bits_words;
+      for (int w0 = jb >> 5; w0 < (je + 31) >> 5; ++w0) {
+        const uint32_t word = (row_ok && lh == 0) ? rbits[w0] : 0u;
+        for (int bit = 0; bit < 32; ++bit) {
+          const int u = 32 * w0 + bit - jb;
+          const uint32_t m = (uint32_t)__ballot((word >> bit) & 1u);
+          if (u >= 0 && u < span && lane == 0) s_bits[UNW * u + wave] = m;
+        }
+      }
+    } else {
+      for (int e = tid; e < span * UNW; e += UNT) s_bits[e] = 0u;
+    }
     __syncthreads();
-    if (my_row < n_rows) {
+    if (video && my_row < n_rows) {
       // entries in [jb, je): binary search for both ends (lists are ascending)
       int lo = 0, hi = my_cnt;
       while (lo < hi) { const int mid = (lo + hi) >> 1; if (my_list[mid] < jb) lo = mid + 1; else hi = mid; }

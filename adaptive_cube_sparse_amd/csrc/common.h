@@ -299,7 +299,9 @@ struct AttnArgs {
   const int32_t* sel_idx;
   void* out_raster;
   void* out_extra;
-  float* partials;  // workspace for split extra rows
+  float* partials;       // workspace: split extra-row partials (when chunked)
+  uint32_t* extra_bits;  // workspace: selection bitmap of extra rows [Hq*n_extra][bits_words]
+  int bits_words;        // ceil(Nc / 32)
   int n_extra;
   int n_text_kv;
   int64_t capv;
@@ -312,6 +314,7 @@ struct AttnArgs {
 };
 void plan_attention(AttnArgs& a, adas_dtype dt);
 size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt);
+void bind_attention_workspace(AttnArgs& a, adas_dtype dt, void* ws);
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s);
 template <int D>
 hipError_t launch_union(const AttnArgs& a, hipStream_t s);

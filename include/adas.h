@@ -177,7 +177,9 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
  * Selected ids must be ascending, < the row's candidate count, and counts
  * must not exceed it; the host does not read device lists (undefined
  * behaviour otherwise).  Outputs are float32-accumulated, stored in dtype.
- * Errors: NULL, SHAPE, VALUE, DTYPE, WORKSPACE, HIP.
+ * The bf16 path with extra rows keeps a per-row selection bitmap and, when it
+ * splits the extra rows' cubes into chunks, their partial results in ws.
+ * Errors: NULL, SHAPE (Nc > ADAS_MAX_CUBES, ...), VALUE, DTYPE, WORKSPACE, HIP.
  */
 adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
                                  const void* k_cube, const void* v_cube, int32_t n_extra,
