@@ -19,38 +19,61 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Merge split partial results of extra rows: one wave per row.
 // Partials of tile t, chunk q, row r sit at ((t * chunks + q) * TR + r) * (D + 2):
-// the row's log2-domain max, its sum, then D unnormalised outputs.
+// the row's log2-domain max, its sum, then D unnormalised outputs.  One
+// workgroup (4 waves) per row: the chunk maxima are reduced first, then each
+// wave folds every fourth chunk (lanes own D/64 output dims, loads unrolled so
+// several chunks are in flight), and the four waves are summed through LDS.
 template <int D, int TR>
 __global__ __launch_bounds__(256) void k_merge_bf16(AttnArgs a, int n_tiles) {
+  constexpr int PER = D / kWave;
+  __shared__ float red_m[4];
+  __shared__ float red_o[4][D + 1];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int tile = wid / TR, r = wid % TR;
+  const int wave = threadIdx.x / kWave;
+  const int tile = blockIdx.x / TR, r = blockIdx.x % TR;
   if (tile >= n_tiles) return;
   const int grp = tile / a.extra_tiles_per_group;
   const int rho = (tile - grp * a.extra_tiles_per_group) * TR + r;
   const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
-  if (rho >= gsz * a.n_extra) return;
+  if (rho >= gsz * a.n_extra) return;  // uniform over the workgroup
   const int slot = rho / a.n_extra;
   const int hq = a.hg.heads[a.hg.start[grp] + slot];
   const int m = rho - slot * a.n_extra;
-  const float* base = a.partials + (size_t)tile * a.extra_chunks * TR * (D + 2);
+  const int chunks = a.extra_chunks;
+  const size_t stride = (size_t)TR * (D + 2);
+  const float* base = a.partials + ((size_t)tile * chunks * TR + r) * (D + 2);
   float M = -INFINITY;
-  for (int q = 0; q < a.extra_chunks; ++q) M = fmaxf(M, base[((size_t)q * TR + r) * (D + 2)]);
-  constexpr int PER = D / kWave;
+  for (int q = threadIdx.x; q < chunks; q += blockDim.x) M = fmaxf(M, base[q * stride]);
+  M = wave_max(M);
+  if (lane == 0) red_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   float o[PER] = {};
   float L = 0.f;
-  for (int q = 0; q < a.extra_chunks; ++q) {
-    const float* p = base + ((size_t)q * TR + r) * (D + 2);
-    const float mq = p[0];
-    if (mq == -INFINITY) continue;
-    const float w = exp2_fast(mq - M);
-    L = fmaf(w, p[1], L);
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int q = wave; q < chunks; q += 4) {
+      const float* p = base + q * stride;
+      const float mq = p[0];
+      const float w = mq == -INFINITY ? 0.f : exp2_fast(mq - M);
+      L = fmaf(w, p[1], L);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = fmaf(w, p[2 + lane * PER + i], o[i]);
+      for (int i = 0; i < PER; ++i) o[i] = fmaf(w, p[2 + lane * PER + i], o[i]);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) red_o[wave][lane * PER + i] = o[i];
+  if (lane == 0) red_o[wave][D] = L;
+  __syncthreads();
+  if (wave != 0) return;
+  const float Lt = red_o[0][D] + red_o[1][D] + red_o[2][D] + red_o[3][D];
   uint16_t* dst = (uint16_t*)a.out_extra + ((size_t)m * a.g.Hq + hq) * D + lane * PER;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[i] = f32_to_bf16_bits(o[i] / L);
+  for (int i = 0; i < PER; ++i) {
+    const int d = lane * PER + i;
+    const float v = red_o[0][d] + red_o[1][d] + red_o[2][d] + red_o[3][d];
+    dst[i] = f32_to_bf16_bits(v / Lt);
+  }
 }
 
 // Selection bitmap of the extra rows: one workgroup per row (hq, m) turns the
@@ -177,8 +200,21 @@ void plan_attention(AttnArgs& a, adas_dtype dt) {
   a.extra_tiles_per_group = 0;
   a.extra_chunks = 1;
   a.extra_chunk_cubes = a.g.Nc;
+  a.decode_chunks = 0;
   a.bits_words = (a.g.Nc + 31) / 32;
   if (dt != ADAS_BF16 || a.n_extra == 0) return;
+  if (!a.has_video && a.hg.gmax * a.n_extra <= 32 && a.g.S % 64 == 0) {
+    // decode mode: k_attn_decode, one workgroup per (KV head, chunk), about two
+    // per CU; every wave of a chunk leaves its own partial row
+    const int want = (512 + a.g.Hkv - 1) / a.g.Hkv;
+    int cubes = (a.g.Nc + want - 1) / want;
+    cubes = ((cubes + decode_waves() - 1) / decode_waves()) * decode_waves();
+    a.extra_chunk_cubes = cubes;
+    a.decode_chunks = (a.g.Nc + cubes - 1) / cubes;
+    a.extra_tiles_per_group = 1;
+    a.extra_chunks = a.decode_chunks * decode_waves();
+    return;
+  }
   const int TR = union_tile_rows();
   a.extra_tiles_per_group = (a.hg.gmax * a.n_extra + TR - 1) / TR;
   const int extra_tiles = a.g.Hkv * a.extra_tiles_per_group;
@@ -204,7 +240,7 @@ size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt) {
   if (dt != ADAS_BF16 || a.n_extra == 0) return 0;
   size_t bytes = bitmap_bytes(a);
   if (a.extra_chunks > 1) {
-    const int TR = union_tile_rows();
+    const int TR = a.decode_chunks > 0 ? 32 : union_tile_rows();
     bytes += (size_t)a.g.Hkv * a.extra_tiles_per_group * a.extra_chunks * TR * (a.g.D + 2) * sizeof(float);
   }
   return bytes;
@@ -225,18 +261,27 @@ hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s) {
       const hipError_t eb = hipGetLastError();
       if (eb != hipSuccess) return eb;
     }
+    if (a.decode_chunks > 0) {
+      hipError_t e = launch_decode(a, s);
+      if (e != hipSuccess) return e;
+      const int rows = a.g.Hkv * 32;
+      if (a.g.D == 128)
+        hipLaunchKernelGGL((k_merge_bf16<128, 32>), dim3(rows), dim3(256), 0, s, a, a.g.Hkv);
+      else
+        hipLaunchKernelGGL((k_merge_bf16<64, 32>), dim3(rows), dim3(256), 0, s, a, a.g.Hkv);
+      return hipGetLastError();
+    }
     hipError_t e = a.g.D == 128 ? launch_union<128>(a, s) : launch_union<64>(a, s);
     if (e != hipSuccess) return e;
     if (a.n_extra > 0 && a.extra_chunks > 1) {
       const int n_tiles = a.g.Hkv * a.extra_tiles_per_group;
       constexpr int TRU = 256;
-      static_assert(TRU % 4 == 0, "four rows per merge workgroup");
       if (union_tile_rows() != TRU) return hipErrorInvalidValue;
-      const int waves = n_tiles * TRU;
+      const int rows = n_tiles * TRU;
       if (a.g.D == 128)
-        hipLaunchKernelGGL((k_merge_bf16<128, TRU>), dim3((waves + 3) / 4), dim3(256), 0, s, a, n_tiles);
+        hipLaunchKernelGGL((k_merge_bf16<128, TRU>), dim3(rows), dim3(256), 0, s, a, n_tiles);
       else
-        hipLaunchKernelGGL((k_merge_bf16<64, TRU>), dim3((waves + 3) / 4), dim3(256), 0, s, a, n_tiles);
+        hipLaunchKernelGGL((k_merge_bf16<64, TRU>), dim3(rows), dim3(256), 0, s, a, n_tiles);
       e = hipGetLastError();
     }
     return e;

@@ -1,0 +1,198 @@
+// Attention for extra rows that fit one wave: decode steps (AdaSpark,
+// papernotes.org, key design 2; a decode query attends to its Top-p cube set
+// only).  When a KV head's extra rows number at most 32 (e.g. one decode token
+// x 7 query heads), the bf16 path uses this kernel instead of union tiles.
+//
+// One workgroup (4 waves) per (KV head, chunk of cubes).  Every wave holds the
+// same <= 32 rows (query operand and float32 accumulators in registers) and
+// walks its own cubes of the chunk (cube c0 + wave, + 4, ...), skipping cubes no
+// row selected.  Each wave owns one LDS block buffer: a key block (64 keys of
+// K rows and V^T rows, values in ADAS_LAYOUT_VT) arrives there by
+// global_load_lds_dwordx4 in 1 KB contiguous pieces, then feeds the MFMAs with
+// the same conflict-free b128 fragment reads as the union kernel.  Waves never
+// share data, so there is no barrier; the four waves of a CU overlap one
+// another's loads and math.  Each wave writes its own partial (max, sum,
+// outputs) row, and k_merge_bf16 combines chunks x waves.
+#include "common.h"
+
+namespace adas {
+
+namespace {
+typedef __bf16 dbf16x8 __attribute__((ext_vector_type(8)));
+typedef float df32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
+constexpr float kLog2eD = 1.4426950408889634f;
+constexpr float kLazyD = 8.0f;  // rescale only when a block max exceeds the reference by 2^8
+constexpr int DW = 4;           // waves per workgroup
+}  // namespace
+
+int decode_waves() { return DW; }
+
+// Requires S % 64 == 0 and at most 32 rows per KV head (host checks).
+template <int D>
+__global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
+  const KGeom& g = a.g;
+  const int n_chunks = a.decode_chunks;
+  const int grp = blockIdx.x / n_chunks;
+  const int chunk = blockIdx.x - grp * n_chunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int hstart = a.hg.start[grp];
+  const int n_rows = (a.hg.start[grp + 1] - hstart) * a.n_extra;
+  const bool row_ok = lr < n_rows;
+  int hq = 0, m = 0;
+  if (row_ok) {
+    const int slot = lr / a.n_extra;
+    hq = a.hg.heads[hstart + slot];
+    m = lr - slot * a.n_extra;
+  }
+  dbf16x8 qb[D / 16];
+  {
+    const uint16_t* src = (const uint16_t*)a.q_extra + ((size_t)m * g.Hq + hq) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(src + 16 * ds + 8 * lh);
+      qb[ds] = __builtin_bit_cast(dbf16x8, v);
+    }
+  }
+  const float qscale = kLog2eD / sqrtf((float)D);
+  const dbf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float m_run = -INFINITY, l_run = 0.f;
+  df32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  // this wave's LDS block: K rows (D + 8 bf16) then V^T rows (64 + 8 bf16)
+  constexpr int KS = D + 8, VS = 64 + 8;
+  constexpr int KPR = D / 8 + 1;             // 16-byte pieces per padded K row
+  constexpr int VPR = 64 / 8 + 1;            // pieces per padded V^T row
+  constexpr int NKI = 64 * KPR / 64;         // K load instructions per block
+  constexpr int NVI = D * VPR / 64;          // V^T load instructions per block
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[DW][64 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[DW][D * VS];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint16_t* mk = lds_k[wv];
+  uint16_t* mv = lds_v[wv];
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  const uint32_t* rbits = a.extra_bits + (size_t)(hq * a.n_extra + m) * a.bits_words;
+  const char* kg = (const char*)a.k_cube + (size_t)grp * g.N * D * 2;
+  const char* vg = (const char*)a.v_cube + (size_t)grp * g.N * D * 2;  // [Nc][D][S]
+  const int c0 = chunk * a.extra_chunk_cubes;
+  const int c1 = min(g.Nc, c0 + a.extra_chunk_cubes);
+  for (int j = c0 + wv; j < c1; j += DW) {
+    const uint32_t bit = (row_ok && lh == 0) ? (rbits[j >> 5] >> (j & 31)) & 1u : 0u;
+    const uint32_t mask = (uint32_t)__ballot(bit != 0u);  // rows of the wave that selected j
+    if (mask == 0u) continue;
+    const bool rowsel = ((mask >> lr) & 1u) != 0u;
+    for (int kb = 0; kb < g.S; kb += 64) {
+      // piece e = 64*q + lane of the padded block; the padding column re-reads
+      // the row's first piece
+      const char* kblk = kg + ((size_t)j * g.S + kb) * D * 2;
+      const char* vblk = vg + (size_t)j * g.S * D * 2 + kb * 2;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous block's LDS reads are done
+#pragma unroll
+      for (int q = 0; q < NKI; ++q) {
+        const int e = 64 * q + lane;
+        const int row = e / KPR, col = e % KPR;
+        __builtin_amdgcn_global_load_lds((const void*)(kblk + row * D * 2 + (col == KPR - 1 ? 0 : col * 16)),
+                                         (lds_void*)((char*)mk + 1024 * q), 16, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < NVI; ++q) {
+        const int e = 64 * q + lane;
+        const int row = e / VPR, col = e % VPR;
+        __builtin_amdgcn_global_load_lds((const void*)(vblk + (size_t)row * g.S * 2 + (col == VPR - 1 ? 0 : col * 16)),
+                                         (lds_void*)((char*)mv + 1024 * q), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the block is in LDS
+      // S^T = K Q^T; keys of st[h2][i]: 32*h2 + 8*(i/4) + 4*lh + (i%4)
+      df32x16 st[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[h2][i] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+          const dbf16x8 ka = __builtin_bit_cast(
+              dbf16x8, *reinterpret_cast<const uint4*>(&mk[(32 * h2 + lr) * KS + 16 * ds + 8 * lh]));
+          st[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ds], st[h2], 0, 0, 0);
+        }
+      }
+      // online softmax in log2 units with lazy rescaling
+      float mb = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mb = fmaxf(fmaxf(mb, st[0][i]), st[1][i]);
+      mb = fmaxf(mb, xor32_f32(mb));
+      const float mb_c = rowsel ? mb * qscale : -INFINITY;
+      const bool grow = mb_c > m_run + kLazyD;
+      if (__ballot(grow) != 0ull) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mb_c) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        m_run = grow ? mb_c : m_run;
+      }
+      const float bias = (rowsel && m_run != -INFINITY) ? m_run : INFINITY;
+      dbf16x8 pb[4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          pb[2 * h2 + i / 8][i % 8] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[h2][i], qscale, -bias));
+      float ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const dbf16x2 pair = {pb[u][2 * e], pb[u][2 * e + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, ls, false);
+        }
+      ls += xor32_f32(ls);
+      l_run += ls;
+      // O^T += V^T P^T; slot 8*lh + e of k-step u holds key 16*u + 8*(e/4) + 4*lh + (e%4),
+      // kept by ADAS_LAYOUT_VT in column 16*u + 8*lh + e
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const dbf16x8 va = __builtin_bit_cast(
+              dbf16x8, *reinterpret_cast<const uint4*>(&mv[(32 * db + lr) * VS + 16 * u + 8 * lh]));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], acc[db], 0, 0, 0);
+        }
+    }
+  }
+  // partial row: [grp][chunk * DW + wave][32 rows][D + 2]
+  if (!row_ok) return;
+  float* dst = a.partials + (((size_t)grp * a.extra_chunks + (size_t)chunk * DW + wave) * 32 + lr) * (D + 2);
+  if (lh == 0) {
+    dst[0] = m_run;
+    dst[1] = l_run;
+  }
+  // acc[db][i] = O^T[d = 32*db + 8*(i/4) + 4*lh + (i%4)][row]
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float* p = dst + 2 + 32 * db + 8 * q + 4 * lh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = acc[db][4 * q + e];
+    }
+}
+
+hipError_t launch_decode(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.g.Hkv * a.decode_chunks));
+  if (a.g.D == 128)
+    hipLaunchKernelGGL((k_attn_decode<128>), grid, dim3(64 * DW), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_decode<64>), grid, dim3(64 * DW), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace adas

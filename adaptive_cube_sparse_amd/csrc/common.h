@@ -309,8 +309,9 @@ struct AttnArgs {
   int has_video;
   // schedule (filled by plan_attention)
   int extra_tiles_per_group;
-  int extra_chunks;
+  int extra_chunks;       // partial rows per tile row (chunks, times waves in decode mode)
   int extra_chunk_cubes;
+  int decode_chunks;      // > 0: extra rows run in k_attn_decode with this many chunks per KV head
 };
 void plan_attention(AttnArgs& a, adas_dtype dt);
 size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt);
@@ -319,5 +320,7 @@ hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s);
 template <int D>
 hipError_t launch_union(const AttnArgs& a, hipStream_t s);
 int union_tile_rows();  // rows per tile of the union kernel
+hipError_t launch_decode(const AttnArgs& a, hipStream_t s);
+int decode_waves();     // waves per workgroup of the decode kernel
 
 }  // namespace adas

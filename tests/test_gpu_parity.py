@@ -77,6 +77,16 @@ def test_decode_rows_split():
     _case(wl)
 
 
+def test_decode_mode_32_rows_uneven_groups_s128():
+    # at most 32 extra rows per KV head run in the per-wave decode kernel: here
+    # exactly 32 (4 heads x 8 tokens) on KV head 0 and 8 on KV head 1, with
+    # 128-token cubes (two key blocks per cube)
+    wl = workloads.Workload(name="decode_32", T=32, H=16, W=16, ct=2, ch=8, cw=8,
+                            n_q_heads=5, n_kv_heads=2, head_dim=128, dtype="bf16", p=0.8,
+                            seed=36, video_queries=False, n_decode=8)
+    _case(wl, head_map=[0, 0, 1, 0, 0])
+
+
 def test_many_cubes_small_cube():
     # Nc = 1152 > 1024 candidates (wide selection path), S = 16 (partial key blocks)
     wl = workloads.Workload(name="many_cubes", T=72, H=16, W=16, ct=1, ch=4, cw=4,
