@@ -156,12 +156,12 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
   if (sel_cap < need)
     return fail(ADAS_ERR_CAPACITY, "sel_cap %lld < required %lld", (long long)sel_cap,
                 (long long)need);
-  const size_t ws_need = adas::select_workspace_bytes(g, dtype);
+  const size_t ws_need = adas::select_workspace_bytes(g, dtype, n_extra, hg.gmax);
   if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need))
     return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_need);
   adas::SelectArgs a;
   a.g = g;
-  a.kbar_split = ws;
+  a.zbuf = (float*)ws;
   a.hg = hg;
   a.q_cube = q_cube;
   a.q_extra = q_extra;
@@ -236,7 +236,8 @@ size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kin
     adas::KGeom g;
     adas::HeadGroups hg;
     if (derive(geom, g, hg) != ADAS_OK || check_dtype(dtype) != ADAS_OK) return 0;
-    return adas::select_workspace_bytes(g, dtype);
+    if (n_extra < 0) return 0;
+    return adas::select_workspace_bytes(g, dtype, n_extra, hg.gmax);
   }
   adas::AttnArgs a;
   const int dummy = 1;

@@ -274,7 +274,7 @@ struct SelectArgs {
   const void* q_cube;   // may be null
   const void* q_extra;  // may be null
   const float* kbar;
-  void* kbar_split;  // workspace: three bf16 planes of kbar (bf16 path)
+  float* zbuf;  // workspace: extra-row logits [Hq*n_extra][Nc] (split selection)
   int n_extra;
   float p;
   int32_t* sel_count;
@@ -284,7 +284,8 @@ struct SelectArgs {
   int has_video;
 };
 hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s);
-size_t select_workspace_bytes(const KGeom& g, adas_dtype dt);
+size_t select_workspace_bytes(const KGeom& g, adas_dtype dt, int n_extra, int gmax);
+bool use_split_select(const KGeom& g, int n_extra, int gmax);
 
 struct AttnArgs {
   KGeom g;

@@ -12,6 +12,10 @@
 //            serves all RT rows; logits land in LDS.
 //   phase B  per row (one wave): max, exp, sum, then the Top-p threshold
 //            search and ascending compaction of topp_select_row().
+// Extra rows with more than 1024 candidates (decode over a long cache) are few
+// and each needs every kbar row, so they take a split path instead: a grid of
+// (KV head, 64-cube chunk) workgroups writes their float32 logits to the
+// workspace, then one wave per row runs the same softmax and Top-p search.
 // f32 path: one wave per row, float32 dot products on the vector ALUs.
 #include <algorithm>
 #include <utility>
@@ -95,6 +99,13 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& 
 }
 
 constexpr int kSelWaves = 8;
+
+// The split path serves extra rows with more than 1024 candidates when a KV
+// head has few of them (at most 64, e.g. decode steps); many extra rows fill
+// the GPU through the fused kernel's row tiles instead.
+bool use_split_select(const KGeom& g, int n_extra, int gmax) {
+  return n_extra > 0 && g.Nc > 1024 && gmax * n_extra <= 64;
+}
 
 // RT rows per tile (a multiple of 16, or 8), NPL candidate slots per lane
 // (capacity 64 * NPL).  Eight waves share every kbar load across RT rows.
@@ -212,6 +223,247 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
   }
 }
 
+// Split selection, step 1: logits of the extra rows of KV head blockIdx.y for
+// candidates 64*blockIdx.x .. +64.  The kbar chunk sits in LDS (rows padded by
+// one float); thread pairs (row, candidate) take float32 dot products.
+template <int D>
+__global__ __launch_bounds__(256) void k_select_scores(SelectArgs a) {
+  __shared__ float kb[64 * (D + 1)];
+  const KGeom& g = a.g;
+  const int grp = blockIdx.y;
+  const int j0 = 64 * blockIdx.x;
+  const int nj = min(64, g.Nc - j0);
+  const float* src = a.kbar + ((size_t)grp * g.Nc + j0) * D;
+  for (int e = threadIdx.x; e < nj * D; e += blockDim.x) kb[(e / D) * (D + 1) + e % D] = src[e];
+  __syncthreads();
+  const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
+  const int rows = gsz * a.n_extra;
+  const float scale = 1.0f / sqrtf((float)D);
+  for (int e = threadIdx.x; e < rows * 64; e += blockDim.x) {
+    const int rho = e >> 6, jl = e & 63;
+    if (jl >= nj) continue;
+    const RowRef rr = extra_row(a.hg, grp, a.n_extra, rho);
+    const uint16_t* q = (const uint16_t*)a.q_extra + ((size_t)rr.pos * g.Hq + rr.hq) * D;
+    const float* k = &kb[jl * (D + 1)];
+    float s = 0.f;
+#pragma unroll 4
+    for (int d8 = 0; d8 < D / 8; ++d8) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(q + 8 * d8);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        s = fmaf(__uint_as_float(w[t] << 16), k[8 * d8 + 2 * t], s);
+        s = fmaf(__uint_as_float(w[t] & 0xFFFF0000u), k[8 * d8 + 2 * t + 1], s);
+      }
+    }
+    a.zbuf[((size_t)rr.hq * a.n_extra + rr.pos) * g.Nc + j0 + jl] = s * scale;
+  }
+}
+
+// Split selection, step 2: one workgroup (SW waves) per extra row (hq, m).
+// The same Top-p search as topp_select_row(), spread over the workgroup: wave
+// w holds candidates w*C .. w*C + C - 1 (C = 64*NPL, stripe i of lane L is
+// candidate w*C + 64*i + L), mass and count sums go through LDS (two slots
+// used alternately, so one barrier per bisection step), the <= 64 elements
+// left between the bounds are gathered for wave 0 to finish on single
+// registers, and the ascending compaction gives each wave its output offset
+// from the per-wave counts.
+constexpr int SW = 8;  // waves per row in the split path
+
+template <int NPL>
+__global__ __launch_bounds__(64 * SW) void k_select_rows(SelectArgs a) {
+  constexpr int C = kWave * NPL;
+  __shared__ float red_f[2][SW];
+  __shared__ int red_i[2][SW];
+  __shared__ float gath[kWave];
+  __shared__ int n_gath;
+  __shared__ float tau_s;
+  __shared__ int cgt_s[SW], ceq_s[SW];
+  const KGeom& g = a.g;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int row = blockIdx.x;  // hq * n_extra + m
+  const int hq = row / a.n_extra, m = row - hq * a.n_extra;
+  const int n = g.Nc;
+  const float* z = a.zbuf + (size_t)row * n;
+  int slot = 0;
+  // workgroup-wide sum of (x, c); every thread gets the totals
+  auto block_sum = [&](float x, int c, float& xs, int& cs) __attribute__((always_inline)) {
+    x = wave_sum(x);
+    if (lane == 0) {
+      red_f[slot][wave] = x;
+      red_i[slot][wave] = c;
+    }
+    __syncthreads();
+    xs = 0.f;
+    cs = 0;
+#pragma unroll
+    for (int w = 0; w < SW; ++w) {
+      xs += red_f[slot][w];
+      cs += red_i[slot][w];
+    }
+    slot ^= 1;
+  };
+  float E[NPL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = wave * C + kWave * i + lane;
+    E[i] = j < n ? z[j] : -INFINITY;
+    mx = fmaxf(mx, E[i]);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red_f[slot][wave] = mx;
+  __syncthreads();
+  mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < SW; ++w) mx = fmaxf(mx, red_f[slot][w]);
+  slot ^= 1;
+  float zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = wave * C + kWave * i + lane;
+    E[i] = j < n ? fast_exp(E[i] - mx) : -1.0f;
+    zs += j < n ? E[i] : 0.0f;
+  }
+  float Z;
+  int dummy;
+  block_sum(zs, 0, Z, dummy);
+  const int64_t off = extra_list_offset(a.capv, g.Hq, a.n_extra, g.Nc, hq, m);
+  int32_t* out = a.sel_idx + off;
+  if (a.p >= 1.0f) {
+    for (int j = threadIdx.x; j < n; j += blockDim.x) out[j] = j;
+    if (threadIdx.x == 0) a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? g.N : 0) + m] = n;
+    return;
+  }
+  const float target = a.p * Z;
+  // 1. bisection on float bits over all candidates
+  uint32_t lo = 0u, hi = 0x3F800001u;  // mass(E >= lo) >= target > mass(E >= hi)
+  int cnt_lo = n, cnt_hi = 0;
+  float tau = 0.0f;
+  bool found = false;
+  while (cnt_lo - cnt_hi > kWave && hi - lo > 1u) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    const float fm = __uint_as_float(mid);
+    float ms = 0.0f;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const bool ge = E[i] >= fm;
+      ms += ge ? E[i] : 0.0f;
+      cnt += popc64(__ballot(ge));
+    }
+    block_sum(ms, cnt, ms, cnt);
+    if (ms >= target) {
+      lo = mid;
+      cnt_lo = cnt;
+    } else {
+      hi = mid;
+      cnt_hi = cnt;
+    }
+  }
+  if (hi - lo <= 1u) {
+    tau = __uint_as_float(lo);
+    found = true;
+  }
+  if (!found) {
+    // 2. fixed mass at or above hi; gather the (<= 64) elements in [lo, hi)
+    const float flo = __uint_as_float(lo), fhi = __uint_as_float(hi);
+    if (threadIdx.x == 0) n_gath = 0;
+    __syncthreads();
+    float mhi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      mhi += E[i] >= fhi ? E[i] : 0.0f;
+      const bool in = E[i] >= flo && E[i] < fhi;
+      const uint64_t bl = __ballot(in);
+      int base = 0;
+      if (bl != 0ull && lane == 0) base = atomicAdd(&n_gath, popc64(bl));
+      base = __shfl(base, 0, kWave);
+      if (in) gath[base + lanes_below(bl)] = E[i];
+    }
+    block_sum(mhi, 0, mhi, dummy);  // its barrier also publishes gath / n_gath
+    if (wave == 0) {
+      const int ng = n_gath;
+      const float v = lane < ng ? gath[lane] : -1.0f;
+      // 3. bisection on one value per lane below the gather-time bound
+      const int cnt_hi0 = cnt_hi;
+      for (;;) {
+        if (cnt_lo - cnt_hi == 1) {
+          tau = wave_max(v >= __uint_as_float(lo) && v < __uint_as_float(hi) ? v : -1.0f);
+          break;
+        }
+        if (hi - lo <= 1u) {
+          tau = __uint_as_float(lo);
+          break;
+        }
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        const float fm = __uint_as_float(mid);
+        const bool ge = v >= fm;
+        const int cnt = cnt_hi0 + popc64(__ballot(ge));
+        const float ms = mhi + wave_sum(ge ? v : 0.0f);
+        if (ms >= target) {
+          lo = mid;
+          cnt_lo = cnt;
+        } else {
+          hi = mid;
+          cnt_hi = cnt;
+        }
+      }
+      if (lane == 0) tau_s = tau;
+    }
+    __syncthreads();
+    tau = tau_s;
+  }
+  // mass strictly above tau, ties at tau, per-wave counts for the compaction
+  float mgt = 0.0f;
+  int cgt = 0, ceq = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    mgt += E[i] > tau ? E[i] : 0.0f;
+    cgt += popc64(__ballot(E[i] > tau));
+    ceq += popc64(__ballot(E[i] == tau));
+  }
+  if (lane == 0) {
+    cgt_s[wave] = cgt;
+    ceq_s[wave] = ceq;
+  }
+  int ceq_all;
+  block_sum(mgt, ceq, mgt, ceq_all);
+  int keq = ceq_all;
+  if (tau > 0.0f) {
+    int k = (int)ceilf((target - mgt) / tau);
+    if (k < 1) k = 1;
+    if (k < keq) keq = k;
+  }
+  // ties are taken in ascending candidate order: waves below this one first
+  int eq_before = 0, base = 0, total = 0;
+  {
+    int eqb = 0;
+    for (int w = 0; w < SW; ++w) {
+      const int take = max(0, min(ceq_s[w], keq - eqb));
+      const int sel_w = cgt_s[w] + take;
+      if (w < wave) base += sel_w;
+      if (w == wave) eq_before = eqb;
+      total += sel_w;
+      eqb += ceq_s[w];
+    }
+  }
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool eq = E[i] == tau;
+    const uint64_t beq = __ballot(eq);
+    const int eq_rank = eq_seen + lanes_below(beq);
+    const bool sel = (E[i] > tau) || (eq && eq_rank < keq);
+    const uint64_t bs = __ballot(sel);
+    if (sel) out[base + lanes_below(bs)] = wave * C + kWave * i + lane;
+    base += popc64(bs);
+    eq_seen += popc64(beq);
+  }
+  if (threadIdx.x == 0) a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? g.N : 0) + m] = total;
+}
+
 // f32 path: one wave per row.  Candidates are strided over lanes; each lane
 // computes its dot products serially in float32.
 template <int D, int NPL>
@@ -303,7 +555,16 @@ static void launch_bf16_all(const SelectArgs& a, hipStream_t s) {
   // capacity that holds Nc.
   {
     auto r = range(1024, 4096);
-    if (r.second > r.first || cap_extra > 1024) launch_bf16<D, 8, 64>(a, s, r.first, r.second, cap_extra > 1024);
+    const bool split = use_split_select(a.g, a.n_extra, a.hg.gmax);
+    if (r.second > r.first || (cap_extra > 1024 && !split))
+      launch_bf16<D, 8, 64>(a, s, r.first, r.second, cap_extra > 1024 && !split);
+    if (use_split_select(a.g, a.n_extra, a.hg.gmax)) {
+      // split path for the extra rows (workspace holds their logits)
+      hipLaunchKernelGGL((k_select_scores<D>), dim3((Nc + 63) / 64, a.g.Hkv), dim3(256), 0, s, a);
+      const int rows = a.g.Hq * a.n_extra;
+      static_assert(ADAS_MAX_CUBES <= kWave * 8 * SW, "split-path capacity");
+      hipLaunchKernelGGL((k_select_rows<8>), dim3(rows), dim3(64 * SW), 0, s, a);
+    }
   }
   {
     auto r = range(512, 1024);
@@ -346,6 +607,10 @@ hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t select_workspace_bytes(const KGeom&, adas_dtype) { return 0; }
+// Only the split path keeps logits in the workspace.
+size_t select_workspace_bytes(const KGeom& g, adas_dtype dt, int n_extra, int gmax) {
+  if (dt != ADAS_BF16 || !use_split_select(g, n_extra, gmax)) return 0;
+  return (size_t)g.Hq * n_extra * g.Nc * sizeof(float);
+}
 
 }  // namespace adas

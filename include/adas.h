@@ -142,8 +142,11 @@ adas_status adas_cube_mean_keys(const adas_geom* geom, adas_dtype dtype, const v
  *                               extra (hq, m): Hq*CapV + (hq*n_extra + m)*Nc
  *                             Entries past a row's count are not written.
  *   sel_cap  capacity of sel_idx in entries (>= adas_sel_capacity()).
- *   ws, ws_bytes  workspace (adas_workspace_bytes(ADAS_WS_SELECT, ...); this
- *            version needs none, so NULL/0 is accepted).
+ *   ws, ws_bytes  workspace (adas_workspace_bytes(ADAS_WS_SELECT, ...)): the
+ *            bf16 path keeps the extra rows' float32 logits there when a row
+ *            has more than 1024 candidates and a KV head has at most 64
+ *            extra rows (decode steps); otherwise none is needed and NULL/0
+ *            is accepted.
  * Ordering: cubes are ranked by (P descending, cube index ascending); the
  * scores are computed to float32 accuracy from the float32 kbar.
  * Errors: NULL, SHAPE (Nc > ADAS_MAX_CUBES, no rows), VALUE (p, head_map),

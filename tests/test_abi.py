@@ -56,9 +56,15 @@ def test_capacity_and_workspace_closed_forms():
     assert lib.adas_sel_capacity(ctypes.byref(g), 1, 0) == Hq * capv
     assert lib.adas_sel_capacity(ctypes.byref(g), 1, 5) == Hq * capv + Hq * 5 * Nc
     assert lib.adas_sel_capacity(ctypes.byref(g), 0, 5) == Hq * 5 * Nc
-    # the selection keeps its logits on chip and needs no workspace
+    # the selection keeps its logits on chip and needs no workspace ...
     assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_SELECT, 1, 0) == 0
     assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_F32, L.ADAS_WS_SELECT, 1, 0) == 0
+    assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_SELECT, 0, 3) == 0
+    # ... except extra rows over more than 1024 cubes (bf16): their float32 logits
+    big = _geom(T=64, H=64, W=64)  # 16 x 16 x 16 = 4096 cubes
+    assert lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_SELECT, 0, 3) == 6 * 3 * 4096 * 4
+    assert lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_F32, L.ADAS_WS_SELECT, 0, 3) == 0
+    assert lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_SELECT, 1, 0) == 0
     # prefill without extra rows needs no attention workspace
     assert lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_ATTN, 1, 0) == 0
     bad = _geom(ct=3)
@@ -95,6 +101,9 @@ def test_select_rejects_invalid_arguments_on_host():
     assert _select(lib, g, n_extra=3, q_extra=None) == L.ADAS_ERR_NULL
     assert _select(lib, g, kbar=None) == L.ADAS_ERR_NULL
     assert _select(lib, g, cap=10) == L.ADAS_ERR_CAPACITY
+    big = _geom(T=64, H=64, W=64)  # 4096 cubes: extra rows need a logit workspace
+    assert _select(lib, big, q_cube=None, n_extra=3, q_extra=FAKE, ws=None, ws_bytes=0) == L.ADAS_ERR_WORKSPACE
+    assert _select(lib, big, q_cube=None, n_extra=3, q_extra=FAKE, ws_bytes=6 * 3 * 4096 * 4 - 1) == L.ADAS_ERR_WORKSPACE
     big = _geom(T=8, H=16, W=16 * 9, ct=1, ch=1, cw=4)               # 9216 cubes > 4096
     assert _select(lib, big) == L.ADAS_ERR_SHAPE
     # head_map entries must name an existing KV head

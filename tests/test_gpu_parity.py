@@ -87,6 +87,16 @@ def test_decode_mode_32_rows_uneven_groups_s128():
     _case(wl, head_map=[0, 0, 1, 0, 0])
 
 
+@pytest.mark.parametrize("p", [0.5, 1.0])
+def test_decode_split_selection_2048_cubes(p):
+    # few extra rows over more than 1024 cubes take the split selection path
+    # (logits in the workspace, one workgroup per row)
+    wl = workloads.Workload(name="decode_2048", T=512, H=16, W=16, ct=4, ch=4, cw=4,
+                            n_q_heads=5, n_kv_heads=2, head_dim=128, dtype="bf16", p=p,
+                            seed=37, video_queries=False, n_decode=3)
+    _case(wl, head_map=[0, 0, 1, 1, 1])
+
+
 def test_many_cubes_small_cube():
     # Nc = 1152 > 1024 candidates (wide selection path), S = 16 (partial key blocks)
     wl = workloads.Workload(name="many_cubes", T=72, H=16, W=16, ct=1, ch=4, cw=4,
