@@ -44,6 +44,7 @@ constexpr int UTR = 32 * UNW;  // rows per tile
 constexpr int UPASS = 1024;  // cubes per selection-bitmap pass
 constexpr float kLog2eU = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;  // rescale only when a block max exceeds the reference by 2^8
+constexpr float kOver = 16777216.0f;  // 2^24: largest block sum accepted without a block max
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 }  // namespace
@@ -281,39 +282,56 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
           st[h2][i] = ok ? st[h2][i] : -INFINITY;
         }
     }
-    float mb = fmaxf(st[0][0], st[1][0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mb = fmaxf(fmaxf(mb, st[0][i]), st[1][i]);  // v_max3
-    mb = fmaxf(mb, xor32_f32(mb));
-    const float mb_c = rowsel ? mb * qscale : -INFINITY;
-    const bool grow = mb_c > m_run + kLazy;
-    if (__ballot(grow) != 0ull) {
-      // only growing lanes rescale (a lane still at -inf must not form -inf - -inf)
-      const float alpha = grow ? ex2(m_run - mb_c) : 1.0f;  // 0 when m_run = -inf
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m_run = grow ? mb_c : m_run;
-    }
-    const float bias = (rowsel && m_run != -INFINITY) ? m_run : INFINITY;
-    // P in bf16; the row sum is taken over the same bf16 values the PV product
-    // uses (two per v_dot2 against (1, 1)), so numerator and denominator agree.
+    // P in bf16 against the reference m_run; the row sum is taken over the
+    // same bf16 values the PV product uses (two per v_dot2 against (1, 1)),
+    // so numerator and denominator agree.
     bf16x8u pb[4];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pb[2 * h2 + i / 8][i % 8] = (__bf16)ex2(fmaf(st[h2][i], qscale, -bias));
     float ls = 0.f;
+    auto make_p = [&](float bias) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2u pair = {pb[u][2 * e], pb[u][2 * e + 1]};
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ls, false);
+        for (int i = 0; i < 16; ++i) pb[2 * h2 + i / 8][i % 8] = (__bf16)ex2(fmaf(st[h2][i], qscale, -bias));
+      ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2u pair = {pb[u][2 * e], pb[u][2 * e + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ls, false);
+        }
+      ls += xor32_f32(ls);
+    };
+    // Fast path: once a row has a reference, P is formed against it without
+    // a block max; the block is accepted while every row's block sum stays
+    // at most 2^kOver (no P above 2^kOver, nothing near overflow).  Otherwise
+    // (a row's first block, or a block far above its reference) the block
+    // max sets the reference first; it is raised only when it exceeds the
+    // old one by more than 2^kLazy, so the accumulators are rescaled rarely.
+    bool done = false;
+    if (__ballot(rowsel && m_run == -INFINITY) == 0ull) {
+      make_p(rowsel ? m_run : INFINITY);
+      done = __ballot(!(ls <= kOver)) == 0ull;
+    }
+    if (!done) {
+      float mb = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mb = fmaxf(fmaxf(mb, st[0][i]), st[1][i]);  // v_max3
+      mb = fmaxf(mb, xor32_f32(mb));
+      const float mb_c = rowsel ? mb * qscale : -INFINITY;
+      const bool grow = mb_c > m_run + kLazy;
+      if (__ballot(grow) != 0ull) {
+        // only growing lanes rescale (a lane still at -inf must not form -inf - -inf)
+        const float alpha = grow ? ex2(m_run - mb_c) : 1.0f;  // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        m_run = grow ? mb_c : m_run;
       }
-    ls += xor32_f32(ls);
+      make_p((rowsel && m_run != -INFINITY) ? m_run : INFINITY);
+    }
     l_run += ls;
     // O^T += V^T P^T over 4 k-steps of 16 keys; slot 8*lh + e of k-step u
     // holds key 16*u + 8*(e/4) + 4*lh + (e%4), which V^T keeps in column
@@ -577,8 +595,10 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     }
     __syncthreads();
     if constexpr (FULL) {
+      const int nblk = s_nunion * nkb_cube;
+      uint32_t mw_next = nblk > 0 ? s_bits[UNW * s_ulist[0] + wave] : 0u;
       dpipeline(
-          s_nunion * nkb_cube,
+          nblk,
           [&](int i, const char*& kb, const char*& vb) __attribute__((always_inline)) {
             const int ci = i / nkb_cube, kbi = i - ci * nkb_cube;
             const int j = __builtin_amdgcn_readfirstlane(jb + s_ulist[ci]);
@@ -586,8 +606,10 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
             vb = vtg + (size_t)j * g.S * D * 2 + kbi * UKB * 2;
           },
           [&](int i, const uint16_t* kb_, const uint16_t* vb_, int kc) __attribute__((always_inline)) {
-            const int ul = s_ulist[i / nkb_cube];
-            const uint32_t mw = s_bits[UNW * ul + wave];
+            // this wave's row mask of block i was read one block earlier; the
+            // read for block i+1 overlaps this block
+            const uint32_t mw = mw_next;
+            if (i + 1 < nblk) mw_next = s_bits[UNW * s_ulist[(i + 1) / nkb_cube] + wave];
             if (mw == 0u) return;
             const bool sel = ((mw >> lr) & 1u) != 0u;
             compute(kFull{}, kb_, vb_, sel, kc, false, 0);
