@@ -10,10 +10,12 @@ The printed JSON line reports:
   value       effective TFLOP/s = 4 * d * (attended (row, key) pairs) / step
               time, counting only the tokens each row attends (selected
               cubes, own cube, causal text);
-  roofline    the attention kernel alone: algorithmic FLOPs (or bytes for
-              decode) per launch / its mean launch time, timed with HIP events
-              on the launch stream inside the timed region, against the
-              MI355X peak;
+  roofline    the attention call alone (adas_sparse_attn_fwd: the kernels
+              listed under "kernels"): algorithmic FLOPs (or bytes for
+              decode) per call / its mean duration, timed with HIP events on
+              the launch stream inside the timed region, against the MI355X
+              peak; "traffic" is the counter-measured HBM bytes per call when
+              profiles/attn_traffic.json matches the current sources;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -54,9 +56,35 @@ def parse():
     return ap.parse_args()
 
 
+ATTN_SOURCES = ("attn.hip", "attn_union.hip", "attn_decode.hip", "common.h")
+
+
 def source_hash() -> str:
-    path = os.path.join(ROOT, "adaptive_cube_sparse_amd", "csrc", "attn.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 prefix over the sources of the kernels one adas_sparse_attn_fwd
+    call launches (the counters in profiles/ are valid only for these)."""
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "adaptive_cube_sparse_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def attention_kernels(wl, n_extra: int) -> list:
+    """Kernels launched by one adas_sparse_attn_fwd call of this workload (the
+    event-timed attention interval covers exactly these)."""
+    if wl.dtype != "bf16":
+        return [f"adas::k_attn_f32<{wl.head_dim}>"]
+    d = wl.head_dim
+    ks = []
+    if n_extra:
+        ks.append("adas::k_extra_bitmap")
+    rows_per_kv = (wl.n_q_heads // wl.n_kv_heads) * n_extra
+    if not wl.video_queries and rows_per_kv <= 32 and wl.cube_size % 64 == 0:
+        ks += [f"adas::k_attn_decode<{d}>", f"adas::k_merge_bf16<{d}, 32>"]
+    else:
+        ks.append(f"adas::k_attn_union<{d}, {'true' if wl.cube_size % 64 == 0 else 'false'}>")
+        if not wl.video_queries:
+            ks.append(f"adas::k_merge_bf16<{d}, 256>")
+    return ks
 
 
 def traffic_entry(workload: str):
@@ -69,7 +97,7 @@ def traffic_entry(workload: str):
         rec = json.load(open(path)).get(workload)
     except Exception:
         return None
-    if not rec or rec.get("attn_hip_sha256_16") != source_hash():
+    if not rec or rec.get("attn_sources_sha256_16") != source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -263,8 +291,8 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_entry(wl.name),
                 "algorithmic_flops_per_launch": flops_step}
-    roof["kernel"] = "k_attn_bf16" if wl.dtype == "bf16" else "k_attn_f32"
-    roof["launch_ms"] = attn_ms
+    roof["kernels"] = attention_kernels(wl, n_extra)
+    roof["launch_ms"] = attn_ms  # one adas_sparse_attn_fwd call: the kernels above
 
     cpu = None
     if not args.no_cpu_baseline:
