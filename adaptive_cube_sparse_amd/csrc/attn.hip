@@ -204,15 +204,15 @@ void plan_attention(AttnArgs& a, adas_dtype dt) {
   a.bits_words = (a.g.Nc + 31) / 32;
   if (dt != ADAS_BF16 || a.n_extra == 0) return;
   if (!a.has_video && a.hg.gmax * a.n_extra <= 32 && a.g.S % 64 == 0) {
-    // decode mode: k_attn_decode, one workgroup per (KV head, chunk), about two
-    // per CU; every wave of a chunk leaves its own partial row
-    const int want = (512 + a.g.Hkv - 1) / a.g.Hkv;
+    // decode mode: k_attn_decode, one workgroup per (KV head, chunk), about one
+    // per CU; each chunk leaves one partial row per extra row
+    const int want = (256 + a.g.Hkv - 1) / a.g.Hkv;
     int cubes = (a.g.Nc + want - 1) / want;
     cubes = ((cubes + decode_waves() - 1) / decode_waves()) * decode_waves();
     a.extra_chunk_cubes = cubes;
     a.decode_chunks = (a.g.Nc + cubes - 1) / cubes;
     a.extra_tiles_per_group = 1;
-    a.extra_chunks = a.decode_chunks * decode_waves();
+    a.extra_chunks = a.decode_chunks;
     return;
   }
   const int TR = union_tile_rows();

@@ -9,10 +9,11 @@
 // row selected.  Each wave owns one LDS block buffer: a key block (64 keys of
 // K rows and V^T rows, values in ADAS_LAYOUT_VT) arrives there by
 // global_load_lds_dwordx4 in 1 KB contiguous pieces, then feeds the MFMAs with
-// the same conflict-free b128 fragment reads as the union kernel.  Waves never
-// share data, so there is no barrier; the four waves of a CU overlap one
-// another's loads and math.  Each wave writes its own partial (max, sum,
-// outputs) row, and k_merge_bf16 combines chunks x waves.
+// the same conflict-free b128 fragment reads as the union kernel.  Waves share
+// no data while they walk their cubes, so there is no barrier in the loop; the
+// four waves of a CU overlap one another's loads and math.  At the end the
+// waves' (max, sum, outputs) states are merged in LDS into one partial row per
+// (chunk, row), and k_merge_bf16 combines the chunks.
 #include "common.h"
 
 namespace adas {
@@ -168,22 +169,50 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
         }
     }
   }
-  // partial row: [grp][chunk * DW + wave][32 rows][D + 2]
-  if (!row_ok) return;
-  float* dst = a.partials + (((size_t)grp * a.extra_chunks + (size_t)chunk * DW + wave) * 32 + lr) * (D + 2);
-  if (lh == 0) {
-    dst[0] = m_run;
-    dst[1] = l_run;
-  }
-  // acc[db][i] = O^T[d = 32*db + 8*(i/4) + 4*lh + (i%4)][row]
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float* p = dst + 2 + 32 * db + 8 * q + 4 * lh;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = acc[db][4 * q + e];
+  // The four waves' states are merged in LDS (the block buffers are free now)
+  // into one partial row per (KV head, chunk): [grp][chunk][32 rows][D + 2].
+  constexpr int RS = D + 2;
+  static_assert(DW * 32 * RS * 4 <= DW * (64 * KS + D * VS) * 2, "merge area fits the block buffers");
+  float* red = reinterpret_cast<float*>(&lds_k[0][0]);  // [wave][row][RS], spans lds_k then lds_v
+  __syncthreads();  // every wave is done with its block buffer
+  if (row_ok) {
+    float* r = red + ((size_t)wave * 32 + lr) * RS;
+    if (lh == 0) {
+      r[0] = m_run;
+      r[1] = l_run;
     }
+    // acc[db][i] = O^T[d = 32*db + 8*(i/4) + 4*lh + (i%4)][row]
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[2 + 32 * db + 8 * q + 4 * lh + e] = acc[db][4 * q + e];
+  }
+  __syncthreads();
+  // thread t: row t / 8, output dims 16*(t % 8) .. +16 (D = 128) or 8*(t % 8) .. +8 (D = 64)
+  constexpr int PD = D / 8;
+  const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
+  if (row >= n_rows) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < DW; ++w) M = fmaxf(M, red[((size_t)w * 32 + row) * RS]);
+  float L = 0.f, o[PD] = {};
+#pragma unroll
+  for (int w = 0; w < DW; ++w) {
+    const float* r = red + ((size_t)w * 32 + row) * RS;
+    const float wgt = r[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(r[0] - M);
+    L = fmaf(wgt, r[1], L);
+#pragma unroll
+    for (int i = 0; i < PD; ++i) o[i] = fmaf(wgt, r[2 + PD * part + i], o[i]);
+  }
+  float* dst = a.partials + (((size_t)grp * a.extra_chunks + chunk) * 32 + row) * RS;
+  if (part == 0) {
+    dst[0] = M;
+    dst[1] = L;
+  }
+#pragma unroll
+  for (int i = 0; i < PD; ++i) dst[2 + PD * part + i] = o[i];
 }
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s) {
