@@ -224,38 +224,60 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
 }
 
 // Split selection, step 1: logits of the extra rows of KV head blockIdx.y for
-// candidates 64*blockIdx.x .. +64.  The kbar chunk sits in LDS (rows padded by
-// one float); thread pairs (row, candidate) take float32 dot products.
+// candidates 64*blockIdx.x .. +64.  The kbar chunk and the group's (at most
+// 64) query rows sit in LDS as float32 (kbar rows padded by one float);
+// thread pairs (row, candidate) take float32 dot products.
 template <int D>
 __global__ __launch_bounds__(256) void k_select_scores(SelectArgs a) {
   __shared__ float kb[64 * (D + 1)];
+  __shared__ float qs[64 * D];
   const KGeom& g = a.g;
   const int grp = blockIdx.y;
   const int j0 = 64 * blockIdx.x;
   const int nj = min(64, g.Nc - j0);
-  const float* src = a.kbar + ((size_t)grp * g.Nc + j0) * D;
-  for (int e = threadIdx.x; e < nj * D; e += blockDim.x) kb[(e / D) * (D + 1) + e % D] = src[e];
-  __syncthreads();
   const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
-  const int rows = gsz * a.n_extra;
+  const int rows = gsz * a.n_extra;  // <= 64 on this path
+  // 16-byte loads, all issued before any LDS store (the chunk is 64*D floats)
+  const float4* src = reinterpret_cast<const float4*>(a.kbar + ((size_t)grp * g.Nc + j0) * D);
+  constexpr int NV = 64 * D / 4 / 256;
+  float4 v[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    v[u] = e < nj * D / 4 ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int e = threadIdx.x; e < rows * D / 8; e += blockDim.x) {
+    const int rho = e / (D / 8), c8 = e % (D / 8);
+    const RowRef rr = extra_row(a.hg, grp, a.n_extra, rho);
+    const uint4 raw = *reinterpret_cast<const uint4*>((const uint16_t*)a.q_extra +
+                                                      ((size_t)rr.pos * g.Hq + rr.hq) * D + 8 * c8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      qs[rho * D + 8 * c8 + 2 * t] = __uint_as_float(w[t] << 16);
+      qs[rho * D + 8 * c8 + 2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = 4 * (threadIdx.x + 256 * u);
+    float* dst = &kb[(e / D) * (D + 1) + e % D];
+    dst[0] = v[u].x;
+    dst[1] = v[u].y;
+    dst[2] = v[u].z;
+    dst[3] = v[u].w;
+  }
+  __syncthreads();
   const float scale = 1.0f / sqrtf((float)D);
   for (int e = threadIdx.x; e < rows * 64; e += blockDim.x) {
     const int rho = e >> 6, jl = e & 63;
     if (jl >= nj) continue;
-    const RowRef rr = extra_row(a.hg, grp, a.n_extra, rho);
-    const uint16_t* q = (const uint16_t*)a.q_extra + ((size_t)rr.pos * g.Hq + rr.hq) * D;
+    const float* q = &qs[rho * D];
     const float* k = &kb[jl * (D + 1)];
     float s = 0.f;
-#pragma unroll 4
-    for (int d8 = 0; d8 < D / 8; ++d8) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(q + 8 * d8);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        s = fmaf(__uint_as_float(w[t] << 16), k[8 * d8 + 2 * t], s);
-        s = fmaf(__uint_as_float(w[t] & 0xFFFF0000u), k[8 * d8 + 2 * t + 1], s);
-      }
-    }
+#pragma unroll 16
+    for (int d = 0; d < D; ++d) s = fmaf(q[d], k[d], s);
+    const RowRef rr = extra_row(a.hg, grp, a.n_extra, rho);
     a.zbuf[((size_t)rr.hq * a.n_extra + rr.pos) * g.Nc + j0 + jl] = s * scale;
   }
 }
