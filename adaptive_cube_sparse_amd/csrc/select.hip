@@ -568,40 +568,33 @@ static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, 
 
 // Video rows of query cube c have c candidates; split them by capacity so
 // that every launch runs loops sized for its candidates (heaviest first).
+// Each band [lo, hi) gets NPL = hi / 64 slots per lane; extra rows (Nc
+// candidates) go with the band that holds Nc, unless the split path takes them.
 template <int D>
 static void launch_bf16_all(const SelectArgs& a, hipStream_t s) {
   const int Nc = a.g.Nc;
-  const int cap_extra = Nc;  // extra rows' candidate count
-  auto range = [&](int lo, int hi) { return std::make_pair(std::min(lo, Nc), std::min(hi, Nc)); };
-  // [lo, hi) of query cubes handled at each capacity; extra rows go with the
-  // capacity that holds Nc.
-  {
-    auto r = range(1024, 4096);
-    const bool split = use_split_select(a.g, a.n_extra, a.hg.gmax);
-    if (r.second > r.first || (cap_extra > 1024 && !split))
-      launch_bf16<D, 8, 64>(a, s, r.first, r.second, cap_extra > 1024 && !split);
-    if (use_split_select(a.g, a.n_extra, a.hg.gmax)) {
-      // split path for the extra rows (workspace holds their logits)
-      hipLaunchKernelGGL((k_select_scores<D>), dim3((Nc + 63) / 64, a.g.Hkv), dim3(256), 0, s, a);
-      const int rows = a.g.Hq * a.n_extra;
-      static_assert(ADAS_MAX_CUBES <= kWave * 8 * SW, "split-path capacity");
-      hipLaunchKernelGGL((k_select_rows<8>), dim3(rows), dim3(64 * SW), 0, s, a);
-    }
-  }
-  {
-    auto r = range(512, 1024);
-    const bool ex = cap_extra > 512 && cap_extra <= 1024;
-    if (r.second > r.first || ex) launch_bf16<D, 32, 16>(a, s, r.first, r.second, ex);
-  }
-  {
-    auto r = range(256, 512);
-    const bool ex = cap_extra > 256 && cap_extra <= 512;
-    if (r.second > r.first || ex) launch_bf16<D, 32, 8>(a, s, r.first, r.second, ex);
-  }
-  {
-    auto r = range(0, 256);
-    const bool ex = cap_extra <= 256;
-    if (r.second > r.first || ex) launch_bf16<D, 32, 4>(a, s, r.first, r.second, ex);
+  const bool split = use_split_select(a.g, a.n_extra, a.hg.gmax);
+  const bool extra = a.n_extra > 0 && !split;
+  auto band = [&](auto launch, int lo, int hi) {
+    const int l = std::min(lo, Nc), h = std::min(hi, Nc);
+    const bool ex = extra && Nc > lo && Nc <= hi;
+    if (h > l || ex) launch(l, h, ex);
+  };
+  band([&](int l, int h, bool ex) { launch_bf16<D, 8, 64>(a, s, l, h, ex); }, 2048, 4096);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 16, 32>(a, s, l, h, ex); }, 1024, 2048);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 16>(a, s, l, h, ex); }, 768, 1024);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 12>(a, s, l, h, ex); }, 512, 768);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 8>(a, s, l, h, ex); }, 384, 512);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 6>(a, s, l, h, ex); }, 256, 384);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 4>(a, s, l, h, ex); }, 128, 256);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 2>(a, s, l, h, ex); }, 64, 128);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 1>(a, s, l, h, ex); }, 0, 64);
+  if (split) {
+    // split path for the extra rows (workspace holds their logits)
+    hipLaunchKernelGGL((k_select_scores<D>), dim3((Nc + 63) / 64, a.g.Hkv), dim3(256), 0, s, a);
+    const int rows = a.g.Hq * a.n_extra;
+    static_assert(ADAS_MAX_CUBES <= kWave * 8 * SW, "split-path capacity");
+    hipLaunchKernelGGL((k_select_rows<8>), dim3(rows), dim3(64 * SW), 0, s, a);
   }
 }
 
