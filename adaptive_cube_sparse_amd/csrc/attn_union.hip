@@ -41,7 +41,7 @@ constexpr int UKB = 64;      // keys per key block
 constexpr int UNW = 8;       // waves per workgroup
 constexpr int UNT = 64 * UNW;
 constexpr int UTR = 32 * UNW;  // rows per tile
-constexpr int UPASS = 1024;  // cubes per selection-bitmap pass
+constexpr int UPASS = 512;   // cubes per selection-bitmap pass (LDS budget)
 constexpr float kLog2eU = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;  // rescale only when a block max exceeds the reference by 2^8
 constexpr float kOver = 16777216.0f;  // 2^24: largest block sum accepted without a block max
@@ -74,8 +74,10 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // Three K and three V^T block buffers as separate LDS objects, so that the
   // compiler can tell reads of one from asynchronous global->LDS loads into
   // another.
-  __shared__ __attribute__((aligned(16))) uint16_t lk0[UKB * Sm::KS], lk1[UKB * Sm::KS], lk2[UKB * Sm::KS];
-  __shared__ __attribute__((aligned(16))) uint16_t lv0[D * Sm::VS], lv1[D * Sm::VS], lv2[D * Sm::VS];
+  __shared__ __attribute__((aligned(16))) uint16_t lk0[UKB * Sm::KS], lk1[UKB * Sm::KS], lk2[UKB * Sm::KS],
+      lk3[UKB * Sm::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t lv0[D * Sm::VS], lv1[D * Sm::VS], lv2[D * Sm::VS],
+      lv3[D * Sm::VS];
   __shared__ uint32_t s_bits[UPASS * UNW];  // [cube in pass][wave] -> rows of the wave that selected it
   __shared__ uint16_t s_ulist[UPASS];       // cubes of the pass selected by any row
   __shared__ int s_nunion;
@@ -84,12 +86,14 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   auto kbuf_c = [&](auto c) __attribute__((always_inline)) {
     if constexpr (decltype(c)::value == 0) return lk0;
     else if constexpr (decltype(c)::value == 1) return lk1;
-    else return lk2;
+    else if constexpr (decltype(c)::value == 2) return lk2;
+    else return lk3;
   };
   auto vbuf_c = [&](auto c) __attribute__((always_inline)) {
     if constexpr (decltype(c)::value == 0) return lv0;
     else if constexpr (decltype(c)::value == 1) return lv1;
-    else return lv2;
+    else if constexpr (decltype(c)::value == 2) return lv2;
+    else return lv3;
   };
   const KGeom& g = a.g;
   const int tid = threadIdx.x;
@@ -436,36 +440,42 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  // Four buffers, block b in buffer b % 4, one barrier per pair of blocks.
+  // Blocks i, i+1 (i even) land while blocks i-2, i-1 are computed; at the
+  // barrier before blocks i, i+1 every wave is done with blocks i-2, i-1, so
+  // their buffers take blocks i+2, i+3.  The loop is unrolled over both
+  // buffer pairs so that every buffer is named at compile time.
   auto dpipeline = [&](int nb, auto bsrc, auto work) __attribute__((always_inline)) {
     if (nb <= 0) return;
     __syncthreads();  // the previous phase no longer reads any buffer
-    {
-      const char *kb, *vb;
-      bsrc(0, kb, vb);
-      issue(kb, vb, C0{});
-      if (nb > 1) { bsrc(1, kb, vb); issue(kb, vb, C1{}); }
-    }
-    // block i sits in buffer i % 3; the loop is unrolled by three so every
-    // buffer is named at compile time
-    auto step = [&](auto bufc, int i) __attribute__((always_inline)) {
-      constexpr int X = decltype(bufc)::value;
-      using Next = std::integral_constant<int, (X + 2) % 3>;
-      if (i + 1 < nb) __builtin_amdgcn_s_waitcnt(0x0F70 | NLMIN);  // vmcnt(NLMIN): block i landed
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (i + 2 < nb) {
+    auto issue_block = [&](int i, auto bufc) __attribute__((always_inline)) {
+      if (i < nb) {
         const char *kb, *vb;
-        bsrc(i + 2, kb, vb);
-        issue(kb, vb, Next{});
+        bsrc(i, kb, vb);
+        issue(kb, vb, bufc);
       }
-      work(i, kbuf_c(bufc), vbuf_c(bufc), UKB);
     };
-    for (int i = 0; i < nb; i += 3) {
-      step(C0{}, i);
-      if (i + 1 >= nb) break;
-      step(C1{}, i + 1);
+    issue_block(0, C0{});
+    issue_block(1, C1{});
+    issue_block(2, C2{});
+    issue_block(3, C3{});
+    auto pair = [&](auto b0, auto b1, auto n0, auto n1, int i) __attribute__((always_inline)) {
+      // blocks i, i+1 have landed (blocks i+2, i+3 may still be in flight at i = 0)
+      if (i == 0 && nb > 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NLMIN));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (i >= 2) {
+        issue_block(i + 2, n0);
+        issue_block(i + 3, n1);
+      }
+      work(i, kbuf_c(b0), vbuf_c(b0), UKB);
+      if (i + 1 < nb) work(i + 1, kbuf_c(b1), vbuf_c(b1), UKB);
+    };
+    for (int i = 0; i < nb; i += 4) {
+      pair(C0{}, C1{}, C2{}, C3{}, i);
       if (i + 2 >= nb) break;
-      step(C2{}, i + 2);
+      pair(C2{}, C3{}, C0{}, C1{}, i + 2);
     }
   };
 
