@@ -150,8 +150,16 @@ __device__ int topp_select_row(const float (&E)[NPL], int n, float Z, float p,
     return n;
   }
   const float target = p * Z;
-  uint32_t lo = 0u, hi = 0x3F800001u;  // mass(E >= lo) >= target > mass(E >= hi)
-  int cnt_lo = n, cnt_hi = 0;
+  // mass(E >= lo) >= target > mass(E >= hi).  Initial lo: the n candidates
+  // below x0 = (1 - p) Z / (2n) hold less than (1 - p) Z / 2, so mass(E >= x0)
+  // > target; starting there skips the steps that only pass over tiny E.
+  uint32_t lo = __float_as_uint(0.5f * (1.0f - p) * Z / (float)n), hi = 0x3F800001u;
+  int cnt_lo = 0, cnt_hi = 0;
+  {
+    const float f0 = __uint_as_float(lo);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) cnt_lo += popc64(__ballot(E[i] >= f0));
+  }
   float tau = 0.0f;
   bool found = false;
   // 1. full bisection

@@ -359,9 +359,18 @@ __global__ __launch_bounds__(64 * SW) void k_select_rows(SelectArgs a) {
     return;
   }
   const float target = a.p * Z;
-  // 1. bisection on float bits over all candidates
-  uint32_t lo = 0u, hi = 0x3F800001u;  // mass(E >= lo) >= target > mass(E >= hi)
-  int cnt_lo = n, cnt_hi = 0;
+  // 1. bisection on float bits over all candidates, from the bracket
+  //    [x0, 1] with x0 = (1 - p) Z / (2n) (see topp_select_row)
+  uint32_t lo = __float_as_uint(0.5f * (1.0f - a.p) * Z / (float)n), hi = 0x3F800001u;
+  int cnt_lo = 0, cnt_hi = 0;
+  {
+    const float f0 = __uint_as_float(lo);
+    int c0 = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) c0 += popc64(__ballot(E[i] >= f0));
+    float unused;
+    block_sum(0.f, c0, unused, cnt_lo);
+  }
   float tau = 0.0f;
   bool found = false;
   while (cnt_lo - cnt_hi > kWave && hi - lo > 1u) {
