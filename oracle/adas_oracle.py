@@ -48,7 +48,7 @@ import numpy as np
 __all__ = [
     "Geometry", "to_f64", "cube_coords", "partition", "mean_keys",
     "kbar_to_f32", "selection_logits", "softmax", "selection_probabilities",
-    "top_p", "top_p_batch", "select_video_rows", "select_extra_rows",
+    "top_p", "top_k", "top_p_batch", "select_video_rows", "select_extra_rows",
     "attend", "attention_video_row", "attention_extra_row",
     "attention_video_rows", "dense_block_causal",
 ]
@@ -211,6 +211,18 @@ def top_p(P: np.ndarray, p: float) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int32)
 
 
+def top_k(P: np.ndarray, k: int) -> np.ndarray:
+    """The fixed-budget alternative the AdaSpark listing compares Top-p with
+    (thelatestinai.com listing, Table 4, "Top-K" row): the k cubes of largest
+    P, equal P taken lower index first (the same order as Top-p), returned in
+    ascending cube order; fewer than k candidates -> all of them."""
+    n = len(P)
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    order = np.lexsort((np.arange(n), -P))      # -P ascending, then index ascending
+    return np.sort(order[:min(k, n)]).astype(np.int32)
+
+
 def top_p_batch(P: np.ndarray, p: float):
     """``top_p`` applied to every row of P [rows][n] (same n for all rows).
 
@@ -241,8 +253,8 @@ def _kv_head(hq: int, Hq: int, Hkv: int, head_map=None) -> int:
 
 
 def select_video_rows(q_cube, kbar, g: Geometry, p: float, heads=None,
-                      cubes=None, head_map=None):
-    """Top-p sets of video rows.
+                      cubes=None, head_map=None, k=None):
+    """Top-p sets of video rows (Top-k sets when k is given).
 
     q_cube: [Hq][N][d] cube layout; kbar: [Hkv][Nc][d] float64.
     Returns {(hq, pos): ascending int32 array} for the requested heads and
@@ -257,14 +269,19 @@ def select_video_rows(q_cube, kbar, g: Geometry, p: float, heads=None,
         for c in cubes:
             q = to_f64(q_cube[hq, c * g.S:(c + 1) * g.S])
             P = selection_probabilities(q, kb[:c])
+            if k is not None:
+                for r in range(g.S):
+                    out[(hq, c * g.S + r)] = top_k(P[r], k)
+                continue
             _, mask = top_p_batch(P, p)
             for r in range(g.S):
                 out[(hq, c * g.S + r)] = np.nonzero(mask[r])[0].astype(np.int32)
     return out
 
 
-def select_extra_rows(q_extra, kbar, p: float, rows=None, head_map=None):
-    """Top-p sets of text / decode rows (every video cube is a candidate).
+def select_extra_rows(q_extra, kbar, p: float, rows=None, head_map=None, k=None):
+    """Top-p sets of text / decode rows (every video cube is a candidate;
+    Top-k sets when k is given).
 
     q_extra: [Nt][Hq][d]. Returns {(hq, m): ascending int32 array}."""
     Nt, Hq, _ = q_extra.shape
@@ -278,6 +295,10 @@ def select_extra_rows(q_extra, kbar, p: float, rows=None, head_map=None):
             continue
         q = to_f64(q_extra[idx, hq])
         P = selection_probabilities(q, kb)
+        if k is not None:
+            for i, m in enumerate(idx):
+                out[(hq, m)] = top_k(P[i], k)
+            continue
         _, mask = top_p_batch(P, p)
         for i, m in enumerate(idx):
             out[(hq, m)] = np.nonzero(mask[i])[0].astype(np.int32)

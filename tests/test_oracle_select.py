@@ -182,3 +182,75 @@ def test_extra_rows_select_over_all_cubes():
         P = O.selection_probabilities(O.to_f64(data["q_text"][m, hq]), kbar[0])
         assert len(P) == g.n_cubes
         assert S.tolist() == O.top_p(P, 0.9).tolist()
+
+
+# --- Top-K, the fixed-budget strategy of the listing's Table 4 -----------------------
+def _brute_force_topk(P, k):
+    """All k-subsets; the answer is the one of largest mass, ties broken by the
+    lexicographically smallest sorted index tuple."""
+    n = len(P)
+    if k >= n:
+        return list(range(n))
+    best = None
+    for sub in itertools.combinations(range(n), k):
+        key = (-sum(P[list(sub)]), sub)
+        best = key if best is None or key < best else best
+    return list(best[1])
+
+
+def test_topk_matches_subset_enumeration():
+    rng = np.random.default_rng(11)
+    for trial in range(120):
+        n = int(rng.integers(1, 11))
+        P = _random_P(rng, n, float(rng.choice([0.3, 1.0, 2.5])))
+        if trial % 3 == 0:
+            P = np.round(P * 4) / 4 + 1e-3   # coarse values: many exact ties
+            P /= P.sum()
+        k = int(rng.integers(1, n + 2))
+        assert O.top_k(P, k).tolist() == _brute_force_topk(P, k), (P, k)
+
+
+def test_topk_limits_and_ties():
+    P = np.array([0.1, 0.3, 0.2, 0.3, 0.1])
+    assert O.top_k(P, 1).tolist() == [1], "equal P: the lower index first"
+    assert O.top_k(P, 2).tolist() == [1, 3]
+    assert O.top_k(P, 4).tolist() == [0, 1, 2, 3]
+    assert O.top_k(P, 9).tolist() == [0, 1, 2, 3, 4], "fewer candidates than k: all"
+    assert O.top_k(np.zeros(0), 3).tolist() == []
+    n = 37
+    assert O.top_k(np.full(n, 1.0 / n), 10).tolist() == list(range(10)), "uniform: lowest indices"
+    with pytest.raises(ValueError):
+        O.top_k(P, 0)
+
+
+def test_topk_is_nested_and_agrees_with_topp_at_its_own_mass():
+    rng = np.random.default_rng(12)
+    for _ in range(60):
+        n = int(rng.integers(2, 300))
+        P = _random_P(rng, n, 2.0)
+        prev = set()
+        for k in range(1, min(n, 40)):
+            S = set(O.top_k(P, k).tolist())
+            assert prev < S and len(S) == k, "sets grow by one cube per unit of k"
+            prev = S
+        # with distinct P, Top-k is the Top-p set at p = mass of the k largest
+        k = int(rng.integers(1, n))
+        srt = np.sort(P)[::-1]
+        if srt[k - 1] > srt[k]:
+            p = float(np.sum(srt[:k]))
+            assert O.top_p(P, p * (1 - 1e-12)).tolist() == O.top_k(P, k).tolist()
+
+
+def test_topk_rows_select_preceding_cubes_only():
+    wl = workloads.get("tiny").replace(name="tiny_topk")
+    data = workloads.generate(wl)
+    g = O.Geometry.of(wl)
+    q_cube, _ = O.partition(data["q"], g)
+    k_cube, _ = O.partition(data["k"], g)
+    kbar = O.mean_keys(k_cube, g)
+    sel = O.select_video_rows(q_cube, kbar, g, p=0.7, k=3)
+    for (hq, pos), S in sel.items():
+        c = pos // g.S
+        assert len(S) == min(3, c) and all(0 <= j < c for j in S)
+        P = O.selection_probabilities(O.to_f64(q_cube[hq, pos][None]), kbar[0, :c])[0]
+        assert S.tolist() == O.top_k(P, 3).tolist()
