@@ -5,7 +5,7 @@ include/adas.h).  This package is its Python binding (``_lib``) plus
 ``AdasAttention``, which owns the device buffers of one layer and chains the
 four library calls:
 
-    cube partition (Q, K, V) -> cube mean keys -> Top-p selection -> attention
+    cube partition (Q, K, V) -> cube mean keys -> Top-p (or Top-K) selection -> attention
 
 Torch is used for device memory and streams only.
 """
@@ -18,13 +18,14 @@ import torch
 from ._lib import (  # noqa: F401
     ADAS_BF16, ADAS_F32, ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT, ADAS_WS_ATTN, ADAS_WS_SELECT,
     AdasError, Geometry, LIB_PATH,
-    adas_cube_mean_keys, adas_cube_partition, adas_select_topp, adas_sel_capacity,
+    adas_cube_mean_keys, adas_cube_partition, adas_select_topk, adas_select_topp, adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
 )
 
 __all__ = [
     "Geometry", "AdasAttention", "AdasError", "adas_cube_partition", "adas_cube_mean_keys",
-    "adas_select_topp", "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
+    "adas_select_topp", "adas_select_topk", "adas_sparse_attn_fwd", "adas_workspace_bytes",
+    "adas_sel_capacity",
     "adas_version", "load", "LIB_PATH",
 ]
 
@@ -35,12 +36,14 @@ class AdasAttention:
     has_video: video query rows are present (prefill); False for decode.
     n_extra:   text / decode query tokens; n_text_kv: text K/V tokens
                (0 or n_extra).
+    topk:      select the topk most probable cubes per row instead of Top-p.
     """
 
     def __init__(self, geom: Geometry, dtype: torch.dtype, p: float, has_video: bool = True,
-                 n_extra: int = 0, n_text_kv: int = 0, device="cuda"):
+                 n_extra: int = 0, n_text_kv: int = 0, device="cuda", topk: Optional[int] = None):
         load()
         self.geom, self.dtype, self.p = geom, dtype, float(p)
+        self.topk = topk
         self.has_video, self.n_extra, self.n_text_kv = has_video, n_extra, n_text_kv
         g = geom
         dev = torch.device(device)
@@ -77,6 +80,10 @@ class AdasAttention:
         adas_cube_partition(self.geom, q_raster, self.q_cube, None, stream)
 
     def select(self, q_extra: Optional[torch.Tensor] = None, p: Optional[float] = None, stream=None):
+        if self.topk is not None and p is None:
+            adas_select_topk(self.geom, self.q_cube, q_extra, self.kbar, self.topk,
+                             self.sel_count, self.sel_idx, self.ws_select, stream)
+            return
         adas_select_topp(self.geom, self.q_cube, q_extra, self.kbar, self.p if p is None else p,
                          self.sel_count, self.sel_idx, self.ws_select, stream)
 

@@ -26,7 +26,7 @@ ADAS_MAX_HEADS = 128
 ADAS_MAX_CUBES = 4096
 
 EXPORTS = (
-    "adas_cube_partition", "adas_cube_mean_keys", "adas_select_topp",
+    "adas_cube_partition", "adas_cube_mean_keys", "adas_select_topp", "adas_select_topk",
     "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
     "adas_status_string", "adas_last_error", "adas_version",
 )
@@ -62,6 +62,7 @@ def load() -> ctypes.CDLL:
         "adas_cube_partition": (i32, [gp, i32, i32, i32, vp, vp, vp, vp]),
         "adas_cube_mean_keys": (i32, [gp, i32, vp, vp, vp]),
         "adas_select_topp": (i32, [gp, i32, vp, i32, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
+        "adas_select_topk": (i32, [gp, i32, vp, i32, vp, vp, i32, vp, vp, i64, vp, sz, vp]),
         "adas_sparse_attn_fwd": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
                                        vp, vp, sz, vp]),
         "adas_workspace_bytes": (sz, [gp, i32, i32, i32, i32]),
@@ -193,11 +194,7 @@ def adas_cube_mean_keys(geom: Geometry, k_cube: torch.Tensor, kbar: torch.Tensor
     _check(st, "adas_cube_mean_keys")
 
 
-def adas_select_topp(geom: Geometry, q_cube: Optional[torch.Tensor], q_extra: Optional[torch.Tensor],
-                     kbar: torch.Tensor, p: float, sel_count: torch.Tensor, sel_idx: torch.Tensor,
-                     ws: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Top-p cube sets for video rows (q_cube [Hq][N][d]) and extra rows
-    (q_extra [n_extra][Hq][d]); see adas.h for the output layout."""
+def _select(fn, name, geom, q_cube, q_extra, kbar, arg, sel_count, sel_idx, ws, stream):
     lib = load()
     ref = q_cube if q_cube is not None else q_extra
     n_extra = 0 if q_extra is None else q_extra.shape[0]
@@ -207,14 +204,31 @@ def adas_select_topp(geom: Geometry, q_cube: Optional[torch.Tensor], q_extra: Op
     rows = (geom.N if q_cube is not None else 0) + n_extra
     _shape(sel_count, (geom.n_q_heads, rows), "sel_count")
     g, keep = geom._c()
-    st = lib.adas_select_topp(ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, ref.dtype, "q_cube"),
-                              n_extra, _ptr(q_extra, ref.dtype, "q_extra"),
-                              _ptr(kbar, torch.float32, "kbar"), float(p),
-                              _ptr(sel_count, torch.int32, "sel_count"),
-                              _ptr(sel_idx, torch.int32, "sel_idx"), sel_idx.numel(),
-                              _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(),
-                              _stream(stream))
-    _check(st, "adas_select_topp")
+    st = getattr(lib, fn)(ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, ref.dtype, "q_cube"),
+                          n_extra, _ptr(q_extra, ref.dtype, "q_extra"),
+                          _ptr(kbar, torch.float32, "kbar"), arg,
+                          _ptr(sel_count, torch.int32, "sel_count"),
+                          _ptr(sel_idx, torch.int32, "sel_idx"), sel_idx.numel(),
+                          _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+                          _stream(stream))
+    _check(st, name)
+
+
+def adas_select_topp(geom: Geometry, q_cube: Optional[torch.Tensor], q_extra: Optional[torch.Tensor],
+                     kbar: torch.Tensor, p: float, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Top-p cube sets for video rows (q_cube [Hq][N][d]) and extra rows
+    (q_extra [n_extra][Hq][d]); see adas.h for the output layout."""
+    _select("adas_select_topp", "adas_select_topp", geom, q_cube, q_extra, kbar, float(p),
+            sel_count, sel_idx, ws, stream)
+
+
+def adas_select_topk(geom: Geometry, q_cube: Optional[torch.Tensor], q_extra: Optional[torch.Tensor],
+                     kbar: torch.Tensor, k: int, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Top-K cube sets (k most probable candidates); same layout as Top-p."""
+    _select("adas_select_topk", "adas_select_topk", geom, q_cube, q_extra, kbar, int(k),
+            sel_count, sel_idx, ws, stream)
 
 
 def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text, v_text,

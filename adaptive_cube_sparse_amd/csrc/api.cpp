@@ -134,16 +134,20 @@ adas_status adas_cube_mean_keys(const adas_geom* geom, adas_dtype dtype, const v
                     "adas_cube_mean_keys launch");
 }
 
-adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
-                             int32_t n_extra, const void* q_extra, const float* kbar, float p,
-                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
-                             size_t ws_bytes, void* stream) {
+// Shared body of adas_select_topp / adas_select_topk (topk > 0 selects Top-K).
+static adas_status select_common(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                 int32_t n_extra, const void* q_extra, const float* kbar, float p,
+                                 int32_t topk, int32_t* sel_count, int32_t* sel_idx,
+                                 int64_t sel_cap, void* ws, size_t ws_bytes, void* stream,
+                                 const char* name) {
   adas::KGeom g;
   adas::HeadGroups hg;
   adas_status st = derive(geom, g, hg);
   if (st != ADAS_OK) return st;
   if ((st = check_dtype(dtype)) != ADAS_OK) return st;
-  if (!(p > 0.0f && p <= 1.0f)) return fail(ADAS_ERR_VALUE, "p must be in (0, 1] (got %g)", (double)p);
+  if (topk == 0 && !(p > 0.0f && p <= 1.0f))
+    return fail(ADAS_ERR_VALUE, "p must be in (0, 1] (got %g)", (double)p);
+  if (topk < 0) return fail(ADAS_ERR_VALUE, "k must be >= 1 (got %d)", topk);
   if (n_extra < 0) return fail(ADAS_ERR_SHAPE, "n_extra must be >= 0");
   if (q_cube == nullptr && n_extra == 0) return fail(ADAS_ERR_SHAPE, "no query rows");
   if (n_extra > 0 && q_extra == nullptr) return fail(ADAS_ERR_NULL, "q_extra is NULL");
@@ -167,13 +171,31 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
   a.q_extra = q_extra;
   a.kbar = kbar;
   a.n_extra = n_extra;
-  a.p = p;
+  a.p = topk > 0 ? 1.0f : p;
+  a.topk = topk;
   a.sel_count = sel_count;
   a.sel_idx = sel_idx;
   a.capv = capv_of(g, has_video);
   a.rows_per_head = (has_video ? g.N : 0) + n_extra;
   a.has_video = has_video;
-  return hip_status(adas::launch_select(a, dtype, (hipStream_t)stream), "adas_select_topp launch");
+  return hip_status(adas::launch_select(a, dtype, (hipStream_t)stream), name);
+}
+
+adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                             int32_t n_extra, const void* q_extra, const float* kbar, float p,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return select_common(geom, dtype, q_cube, n_extra, q_extra, kbar, p, 0, sel_count, sel_idx,
+                       sel_cap, ws, ws_bytes, stream, "adas_select_topp launch");
+}
+
+adas_status adas_select_topk(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                             int32_t n_extra, const void* q_extra, const float* kbar, int32_t k,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (k < 1) return fail(ADAS_ERR_VALUE, "k must be >= 1 (got %d)", k);
+  return select_common(geom, dtype, q_cube, n_extra, q_extra, kbar, 1.0f, k, sel_count, sel_idx,
+                       sel_cap, ws, ws_bytes, stream, "adas_select_topk launch");
 }
 
 static adas_status build_attn(const adas_geom* geom, adas_dtype dtype, const void* q_cube,

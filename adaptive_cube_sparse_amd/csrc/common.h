@@ -261,6 +261,59 @@ __device__ int topp_select_row(const float (&E)[NPL], int n, float Z, float p,
   return base;
 }
 
+// ---------------------------------------------------------------------------
+// Top-K on one row held by one wave (the fixed-budget strategy the AdaSpark
+// listing compares with Top-p, Table 4): the k candidates of largest logit
+// (P is monotone in the logit), equal logits lower index first.
+//
+// z[i] (lane L) is the logit of candidate j = L + 64*i, valid for j < n.
+// Logits map to unsigned keys that order like the floats; the k-th largest
+// key t is built bit by bit from the top (largest t with count(key >= t) >= k),
+// then the keys above t and the lowest-index ties at t are compacted in
+// ascending order.  Writes the ids to out[0..) and returns their count.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ordered_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <int NPL>
+__device__ int topk_select_row(const float (&z)[NPL], int n, int k, int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (n <= 0) return 0;
+  if (k >= n) {
+    for (int j = lane; j < n; j += kWave) out[j] = j;
+    return n;
+  }
+  uint32_t u[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) u[i] = lane + kWave * i < n ? ordered_key(z[i]) : 0u;  // 0: padding
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) cnt += popc64(__ballot(u[i] >= cand));
+    if (cnt >= k) t = cand;
+  }
+  int cgt = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) cgt += popc64(__ballot(u[i] > t));
+  const int keq = k - cgt;  // ties at t to take, lowest index first
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool eq = u[i] == t;
+    const uint64_t beq = __ballot(eq);
+    const bool sel = u[i] > t || (eq && eq_seen + lanes_below(beq) < keq);
+    const uint64_t bs = __ballot(sel);
+    if (sel) out[base + lanes_below(bs)] = lane + kWave * i;
+    base += popc64(bs);
+    eq_seen += popc64(beq);
+  }
+  return base;
+}
+
 // Column of cube offset r in a value row of ADAS_LAYOUT_VT: bits 2 and 3 of r
 // swapped inside every complete aligned group of 16 offsets, identity in a
 // trailing partial group.  An involution.
@@ -285,6 +338,7 @@ struct SelectArgs {
   float* zbuf;  // workspace: extra-row logits [Hq*n_extra][Nc] (split selection)
   int n_extra;
   float p;
+  int topk;  // > 0: Top-K selection of topk cubes instead of Top-p
   int32_t* sel_count;
   int32_t* sel_idx;
   int64_t capv;  // per-head video capacity (0 without video rows)

@@ -208,17 +208,22 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
       E[i] = j < n ? sZ[row * NCAP + j] : -INFINITY;
       m = fmaxf(m, E[i]);
     }
-    m = wave_max(m);
-    float zs = 0.f;
+    int cnt;
+    if (a.topk > 0) {
+      cnt = topk_select_row<NPL>(E, n, a.topk, a.sel_idx + off);
+    } else {
+      m = wave_max(m);
+      float zs = 0.f;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int j = lane + kWave * i;
-      E[i] = j < n ? fast_exp(E[i] - m) : -1.0f;
-      zs += j < n ? E[i] : 0.0f;
+      for (int i = 0; i < NPL; ++i) {
+        const int j = lane + kWave * i;
+        E[i] = j < n ? fast_exp(E[i] - m) : -1.0f;
+        zs += j < n ? E[i] : 0.0f;
+      }
+      zs = wave_sum(zs);
+      __builtin_amdgcn_wave_barrier();  // all lanes have read the row before it is reused
+      cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off, &sZ[row * NCAP]);
     }
-    zs = wave_sum(zs);
-    __builtin_amdgcn_wave_barrier();  // all lanes have read the row before it is reused
-    const int cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off, &sZ[row * NCAP]);
     if (lane == 0) a.sel_count[(size_t)rr.hq * a.rows_per_head + row_index] = cnt;
   }
 }
@@ -333,6 +338,63 @@ __global__ __launch_bounds__(64 * SW) void k_select_rows(SelectArgs a) {
     const int j = wave * C + kWave * i + lane;
     E[i] = j < n ? z[j] : -INFINITY;
     mx = fmaxf(mx, E[i]);
+  }
+  const int64_t off0 = extra_list_offset(a.capv, g.Hq, a.n_extra, g.Nc, hq, m);
+  if (a.topk > 0) {
+    // Top-K: the k-th largest ordered key, built bit by bit with block-wide
+    // counts, then the keys above it and the lowest-index ties, ascending
+    const int K = a.topk;
+    int32_t* outk = a.sel_idx + off0;
+    if (K >= n) {
+      for (int j = threadIdx.x; j < n; j += blockDim.x) outk[j] = j;
+      if (threadIdx.x == 0) a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? g.N : 0) + m] = n;
+      return;
+    }
+    uint32_t u[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) u[i] = wave * C + kWave * i + lane < n ? ordered_key(E[i]) : 0u;
+    uint32_t t = 0u;
+    float unused;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) c += popc64(__ballot(u[i] >= cand));
+      int call;
+      block_sum(0.f, c, unused, call);
+      if (call >= K) t = cand;
+    }
+    int cgt = 0, ceq = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      cgt += popc64(__ballot(u[i] > t));
+      ceq += popc64(__ballot(u[i] == t));
+    }
+    if (lane == 0) {
+      cgt_s[wave] = cgt;
+      ceq_s[wave] = ceq;
+    }
+    int cgt_all;
+    block_sum(0.f, cgt, unused, cgt_all);
+    const int keq = K - cgt_all;
+    int eqb = 0, basek = 0;
+    for (int w = 0; w < wave; ++w) {
+      basek += cgt_s[w] + max(0, min(ceq_s[w], keq - eqb));
+      eqb += ceq_s[w];
+    }
+    int eq_seen = eqb;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const bool eq = u[i] == t;
+      const uint64_t beq = __ballot(eq);
+      const bool sel = u[i] > t || (eq && eq_seen + lanes_below(beq) < keq);
+      const uint64_t bs = __ballot(sel);
+      if (sel) outk[basek + lanes_below(bs)] = wave * C + kWave * i + lane;
+      basek += popc64(bs);
+      eq_seen += popc64(beq);
+    }
+    if (threadIdx.x == 0) a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? g.N : 0) + m] = K;
+    return;
   }
   mx = wave_max(mx);
   if (lane == 0) red_f[slot][wave] = mx;
@@ -544,6 +606,11 @@ __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_vide
     }
     E[i] = z;
     m = fmaxf(m, z);
+  }
+  if (a.topk > 0) {
+    const int cnt = topk_select_row<NPL>(E, n, a.topk, a.sel_idx + off);
+    if (lane == 0) a.sel_count[(size_t)hq * a.rows_per_head + row_index] = cnt;
+    return;
   }
   m = wave_max(m);
   float zs = 0.f;

@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="select the K most probable cubes per row instead of Top-p (a timing "
+                         "control: fixed budget versus the adaptive one)")
     ap.add_argument("--decode-batch", type=int, default=1,
                     help="decode tokens per step for the decode workload (1 = one step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -146,7 +149,7 @@ def decode_unique_bytes(layer, wl) -> int:
     return kv_bytes + qo + list_entries * 4 + Hq * n_extra * 4
 
 
-def cpu_baseline(wl, data, budget_s: float):
+def cpu_baseline(wl, data, budget_s: float, topk: int = 0):
     """Time the CPU oracle on a bounded, seeded sample of the workload's rows:
     selection softmax + Top-p + attention per row (partition and mean keys of
     the whole input are timed too).  BLAS is pinned to one thread."""
@@ -172,13 +175,13 @@ def cpu_baseline(wl, data, budget_s: float):
                 pos = int(rng.integers(g.N))
                 c = pos // g.S
                 P = O.selection_probabilities(O.to_f64(q_cube[hq, pos]), kbar[hq // rep][:c])
-                S_ = O.top_p(P, wl.p)
+                S_ = O.top_k(P, topk) if topk else O.top_p(P, wl.p)
                 O.attention_video_row(q_cube, k_cube, v_cube, g, hq, pos, S_)
                 keys = (len(S_) + 1) * g.S
             else:
                 m = int(rng.integers(wl.n_decode or wl.n_text))
                 P = O.selection_probabilities(O.to_f64(data["q_text"][m, hq]), kbar[hq // rep])
-                S_ = O.top_p(P, wl.p)
+                S_ = O.top_k(P, topk) if topk else O.top_p(P, wl.p)
                 O.attention_extra_row(data["q_text"], k_cube, v_cube, g, hq, m, S_)
                 keys = len(S_) * g.S
             t_rows += time.perf_counter() - t1
@@ -230,7 +233,7 @@ def main():
     n_extra = wl.n_text + wl.n_decode
     n_text_kv = wl.n_text if wl.text_kv else 0
     layer = AdasAttention(geom, dt, wl.p, has_video=wl.video_queries, n_extra=n_extra,
-                          n_text_kv=n_text_kv, device=dev)
+                          n_text_kv=n_text_kv, device=dev, topk=args.topk or None)
     q = up(data["q"]) if wl.video_queries else None
     k, v = up(data["k"]), up(data["v"])
     qe = up(data["q_text"]) if n_extra else None
@@ -296,7 +299,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, data, args.cpu_seconds)
+        cpu = cpu_baseline(wl, data, args.cpu_seconds, args.topk)
 
     dens = None
     if wl.video_queries:
@@ -310,7 +313,8 @@ def main():
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "grid": [wl.T, wl.H, wl.W],
                    "cube_thw": [wl.ct, wl.ch, wl.cw], "heads": [wl.n_q_heads, wl.n_kv_heads],
-                   "head_dim": wl.head_dim, "p": wl.p, "extra_queries": n_extra,
+                   "head_dim": wl.head_dim, "p": wl.p, "topk": args.topk or None,
+                   "extra_queries": n_extra,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -158,6 +158,21 @@ adas_status adas_select_topp(const adas_geom* geom, adas_dtype dtype, const void
                              size_t ws_bytes, void* stream);
 
 /*
+ * adas_select_topk -- fixed-budget cube sets, the alternative the AdaSpark
+ * listing (thelatestinai.com, Table 4, "Top-K" row) compares Top-p with.
+ * Same rows, candidates, outputs and layout as adas_select_topp, but each
+ * row keeps the k candidates of largest P (equivalently largest logit; equal
+ * values lower cube index first), emitted ascending; a row with at most k
+ * candidates keeps all of them.  Scores are computed as in adas_select_topp.
+ *   k        budget, >= 1
+ * Errors: as adas_select_topp, VALUE for k < 1.
+ */
+adas_status adas_select_topk(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                             int32_t n_extra, const void* q_extra, const float* kbar, int32_t k,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * adas_sparse_attn_fwd -- attention over the selected cubes plus the own cube
  * (papernotes.org, key design 2: always keep full attention to the own cube).
  *

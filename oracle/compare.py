@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .adas_oracle import top_p
+from .adas_oracle import top_k, top_p
 
 TOL_MASS = 1e-5
 TOL_REL = 1e-5
@@ -66,3 +66,23 @@ def grade_rows(items, p: float):
     for P, S in items:
         counts[grade_row(P, p, S)] += 1
     return counts
+
+
+def grade_row_topk(P: np.ndarray, k: int, S_dev, tol_rel: float = TOL_REL) -> str:
+    """Top-K counterpart: ``exact``; ``near_tie`` when the device set has the
+    right size and differs only by cubes whose probability is within
+    ``tol_rel`` (relative) of the oracle's k-th largest; ``fail`` otherwise."""
+    S_dev = np.asarray(S_dev, dtype=np.int64)
+    S_ref = top_k(P, k)
+    if S_dev.shape == S_ref.shape and np.array_equal(S_dev, S_ref):
+        return "exact"
+    n = len(P)
+    if len(S_dev) != len(S_ref) or len(S_dev) == 0:
+        return "fail"
+    if np.any(np.diff(S_dev) <= 0) or S_dev.min() < 0 or S_dev.max() >= n:
+        return "fail"
+    cut = P[S_ref].min()
+    diff = np.setxor1d(S_dev, S_ref)
+    if np.all(np.abs(P[diff] - cut) <= tol_rel * cut):
+        return "near_tie"
+    return "fail"

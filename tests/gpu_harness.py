@@ -19,7 +19,7 @@ import torch
 
 import workloads
 from oracle import adas_oracle as O
-from oracle.compare import grade_row
+from oracle.compare import grade_row, grade_row_topk
 
 TOL_BF16 = (2e-2, 2e-3)   # max-abs, mean-abs
 TOL_F32 = (1e-4, 1e-5)
@@ -49,15 +49,16 @@ def geometry(wl, head_map=None):
                     wl.head_dim, head_map)
 
 
-def run_device(wl, data, p=None, head_map=None, dev="cuda:0"):
-    """Whole path on the device; returns the layer object (tensors stay there)."""
+def run_device(wl, data, p=None, head_map=None, dev="cuda:0", k=None):
+    """Whole path on the device (Top-k selection when k is given); returns the
+    layer object (tensors stay there)."""
     from adaptive_cube_sparse_amd import AdasAttention
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     n_extra = wl.n_text + wl.n_decode
     n_text_kv = wl.n_text if wl.text_kv else 0
     layer = AdasAttention(geometry(wl, head_map), dt, wl.p if p is None else p,
                           has_video=wl.video_queries, n_extra=n_extra, n_text_kv=n_text_kv,
-                          device=dev)
+                          device=dev, topk=k)
     q = to_dev(data["q"], dev) if wl.video_queries else None
     qe = to_dev(data["q_text"], dev) if n_extra else None
     kt = to_dev(data["k_text"], dev) if n_text_kv else None
@@ -159,17 +160,19 @@ def selection_probs(ref: Reference, kind, hq, i):
     return O.selection_probabilities(q, kb)
 
 
-def check_rows(ref: Reference, layer, rows, p, max_mismatch_frac=0.01):
-    """Grade the selection of `rows` and compare their outputs."""
+def check_rows(ref: Reference, layer, rows, p, max_mismatch_frac=0.01, k=None):
+    """Grade the selection of `rows` (Top-p, or Top-k when k is given) and
+    compare their outputs."""
     lists = fetch_lists(ref, layer, rows)
     grades = {"exact": 0, "near_threshold": 0, "near_tie": 0, "fail": 0}
     fails = []
     for (kind, hq, i), S in zip(rows, lists):
         P = selection_probs(ref, kind, hq, i)
-        gr = grade_row(P, p, S)
+        gr = grade_row(P, p, S) if k is None else grade_row_topk(P, k, S)
         grades[gr] += 1
         if gr == "fail" and len(fails) < 5:
-            fails.append((kind, hq, i, S[:10].tolist(), O.top_p(P, p)[:10].tolist()))
+            want = O.top_p(P, p) if k is None else O.top_k(P, k)
+            fails.append((kind, hq, i, S[:10].tolist(), want[:10].tolist()))
     log(f"  selection grades over {len(rows)} rows: {grades}")
     assert grades["fail"] == 0, f"selection failures: {fails}"
     assert grades["near_threshold"] + grades["near_tie"] <= max(2, max_mismatch_frac * len(rows))

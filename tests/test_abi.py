@@ -113,6 +113,23 @@ def test_select_rejects_invalid_arguments_on_host():
     assert _select(lib, g2) == L.ADAS_ERR_VALUE
 
 
+def test_topk_rejects_invalid_arguments_on_host():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _geom()
+
+    def topk(k, **kw):
+        a = dict(q_cube=FAKE, cap=1 << 40)
+        a.update(kw)
+        return lib.adas_select_topk(ctypes.byref(g), L.ADAS_BF16, a["q_cube"], 0, None, FAKE, k,
+                                    FAKE, FAKE, a["cap"], FAKE, 1 << 40, None)
+    for k in (0, -3):
+        assert topk(k) == L.ADAS_ERR_VALUE
+    assert "k must be" in lib.adas_last_error().decode()
+    assert topk(4, cap=10) == L.ADAS_ERR_CAPACITY
+    assert topk(4, q_cube=None) == L.ADAS_ERR_SHAPE
+
+
 def test_attention_and_partition_reject_invalid_arguments_on_host():
     import adaptive_cube_sparse_amd._lib as L
     lib = L.load()

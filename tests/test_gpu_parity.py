@@ -18,16 +18,16 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 
-def _case(wl, p=None, head_map=None, rows="all", **kw):
+def _case(wl, p=None, head_map=None, rows="all", k=None, **kw):
     log(f"case {wl.name}: grid {wl.T}x{wl.H}x{wl.W} cube t{wl.ct}h{wl.ch}w{wl.cw} "
         f"heads {wl.n_q_heads}/{wl.n_kv_heads} d {wl.head_dim} {wl.dtype} p {p or wl.p} "
-        f"extra {wl.n_text + wl.n_decode} head_map {head_map}")
+        f"top-k {k} extra {wl.n_text + wl.n_decode} head_map {head_map}")
     data = workloads.generate(wl)
-    layer = run_device(wl, data, p=p, head_map=head_map)
+    layer = run_device(wl, data, p=p, head_map=head_map, k=k)
     ref = Reference(wl, data, head_map)
     check_layout(ref, layer)
     rws = all_rows(ref) if rows == "all" else sampled_rows(ref, **kw)
-    check_rows(ref, layer, rws, wl.p if p is None else p)
+    check_rows(ref, layer, rws, wl.p if p is None else p, k=k)
     return ref, layer
 
 
@@ -111,6 +111,28 @@ def test_deterministic():
     b = run_device(SMALL, data)
     assert torch.equal(a.sel_count, b.sel_count)
     assert torch.equal(a.out_raster.view(torch.int16), b.out_raster.view(torch.int16))
+
+
+# --- Top-K selection (the listing's Table 4 alternative) -------------------------------
+@pytest.mark.parametrize("k", [1, 5, 40])
+def test_small_bf16_topk(k):
+    # SMALL has 32 cubes: k = 40 keeps every candidate of every row
+    _case(SMALL, k=k)
+
+
+def test_tiny_f32_topk():
+    _case(workloads.get("tiny"), k=3)
+
+
+def test_topk_text_rows_and_split_decode():
+    wl = workloads.Workload(name="text_topk", T=8, H=16, W=16, ct=2, ch=8, cw=8, n_q_heads=4,
+                            n_kv_heads=1, head_dim=128, dtype="bf16", p=0.9, seed=38,
+                            n_text=40, text_kv=True)
+    _case(wl, k=3)
+    wl = workloads.Workload(name="decode_2048_topk", T=512, H=16, W=16, ct=4, ch=4, cw=4,
+                            n_q_heads=5, n_kv_heads=2, head_dim=128, dtype="bf16", p=0.5,
+                            seed=39, video_queries=False, n_decode=3)
+    _case(wl, head_map=[0, 0, 1, 1, 1], k=300)
 
 
 # --- full-size configurations: sampled rows ------------------------------------------
