@@ -31,7 +31,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "generate", "f32_to_bf16_bits",
-    "bf16_bits_to_f32",
+    "bf16_bits_to_f32", "FfnWorkload", "FFN_WORKLOADS", "get_ffn", "generate_ffn",
 ]
 
 
@@ -199,4 +199,116 @@ def generate(wl: Workload) -> dict:
             out["v_text"] = _cast(rng.standard_normal((wl.n_text, Hkv, d), dtype=np.float32), wl.dtype)
     if wl.n_decode:
         out["q_text"] = _cast(rng.standard_normal((wl.n_decode, Hq, d), dtype=np.float32), wl.dtype)
+    return out
+
+
+# --------------------------------------------------------------------------
+# AdaS-FFN inputs (the papernotes.org page, key design 3: tokens of each cube
+# are kept or skipped by their L2 norm; the thelatestinai.com listing, Table 5:
+# Qwen2.5-VL-3B / 7B backbones, whose MLP is SwiGLU)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class FfnWorkload:
+    """One synthetic AdaS-FFN layer input.
+
+    Video hidden states ``x[N][hidden]`` in raster token order on a T x H x W
+    grid cut into ct x ch x cw cubes, optional text hidden states
+    ``x_text[Nt][hidden]``, and SwiGLU weights in the nn.Linear layout:
+    ``w_gate, w_up [inter][hidden]``, ``w_down [hidden][inter]``.
+
+    Token magnitudes vary so that the norm-based selection has something to
+    adapt to: token n is ``exp(s_c * z_n) * u_n`` with ``u_n ~ N(0, I)``,
+    ``z_n ~ N(0, 1)`` and ``s_c`` = ``spread_hi`` for a seeded half of the
+    cubes ("busy" cubes, a few dominant tokens) and ``spread_lo`` for the rest
+    ("flat" cubes, near-uniform norms).
+    """
+    name: str
+    T: int
+    H: int
+    W: int
+    ct: int
+    ch: int
+    cw: int
+    hidden: int
+    inter: int
+    p: float
+    seed: int
+    n_text: int = 0
+    spread_lo: float = 0.2
+    spread_hi: float = 1.0
+    description: str = ""
+
+    @property
+    def n_tokens(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def cube_size(self) -> int:
+        return self.ct * self.ch * self.cw
+
+    @property
+    def n_cubes(self) -> int:
+        return self.n_tokens // self.cube_size
+
+    def replace(self, **kw) -> "FfnWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+FFN_WORKLOADS = {
+    "ffn_tiny": FfnWorkload(name="ffn_tiny", T=4, H=8, W=8, ct=2, ch=4, cw=4, hidden=256, inter=384,
+                            p=0.7, seed=2001, n_text=5,
+                            description="Tiny AdaS-FFN: 4x8x8 grid, cube 4x4x2 (8 cubes of 32), hidden 256, "
+                                        "inter 384, 5 text tokens, p=0.7"),
+    "ffn3b": FfnWorkload(name="ffn3b", T=64, H=16, W=16, ct=4, ch=4, cw=4, hidden=2048, inter=11008,
+                         p=0.7, seed=2002,
+                         description="Qwen2.5-VL-3B-shaped FFN: 64x16x16 grid, cube 4x4x4 (256 cubes of 64), "
+                                     "hidden 2048, inter 11008, p=0.7"),
+    "ffn7b": FfnWorkload(name="ffn7b", T=256, H=16, W=16, ct=4, ch=4, cw=4, hidden=3584, inter=18944,
+                         p=0.7, seed=2003,
+                         description="Qwen2.5-VL-7B-shaped FFN: 256x16x16 grid, cube 4x4x4 (1024 cubes of 64), "
+                                     "hidden 3584, inter 18944, p=0.7"),
+    "ffn_hour": FfnWorkload(name="ffn_hour", T=512, H=16, W=16, ct=2, ch=8, cw=8, hidden=3584, inter=18944,
+                            p=0.9, seed=2004, n_text=256,
+                            description="Hour-scale FFN: 512x16x16 grid, cube 8x8x2 (1024 cubes of 128), "
+                                        "hidden 3584, inter 18944, p=0.9, +256 text tokens"),
+}
+
+
+def get_ffn(name: str, **overrides) -> FfnWorkload:
+    wl = FFN_WORKLOADS[name]
+    return wl.replace(**overrides) if overrides else wl
+
+
+def generate_ffn(wl: FfnWorkload) -> dict:
+    """Draw every input of ``wl`` as bf16 bits.
+
+    Draw order from ``np.random.Generator(PCG64(seed))``: a permutation of the
+    cube slots (its first half are the busy cubes); per-token log-magnitudes
+    ``z (N,)``; directions ``u (N, hidden)``; text states ``(Nt, hidden)``;
+    ``w_gate``, ``w_up`` ``(inter, hidden)`` scaled by 1/sqrt(hidden);
+    ``w_down`` ``(hidden, inter)`` scaled by 1/sqrt(inter).  All float32
+    standard normals, rounded to bf16 (RNE).
+    """
+    if wl.T % wl.ct or wl.H % wl.ch or wl.W % wl.cw:
+        raise ValueError("cube extents must divide the grid")
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    nT, nH, nW = wl.T // wl.ct, wl.H // wl.ch, wl.W // wl.cw
+    N, Hd, I = wl.n_tokens, wl.hidden, wl.inter
+    order = rng.permutation(nT * nH * nW)
+    spread = np.full(nT * nH * nW, wl.spread_lo, dtype=np.float32)
+    spread[order[: (nT * nH * nW) // 2]] = wl.spread_hi
+    spread_tok = _expand_cubes(spread.reshape(nT, nH, nW), wl)          # (N,)
+    z = rng.standard_normal(N, dtype=np.float32)
+    mag = np.exp(spread_tok * z).astype(np.float32)
+    out = {"workload": wl}
+    u = rng.standard_normal((N, Hd), dtype=np.float32)
+    u *= mag[:, None]
+    out["x"] = f32_to_bf16_bits(u)
+    del u
+    out["x_text"] = f32_to_bf16_bits(rng.standard_normal((wl.n_text, Hd), dtype=np.float32))
+    for name, shape, fan_in in (("w_gate", (I, Hd), Hd), ("w_up", (I, Hd), Hd), ("w_down", (Hd, I), I)):
+        w = rng.standard_normal(shape, dtype=np.float32)
+        w *= np.float32(1.0 / np.sqrt(fan_in))
+        out[name] = f32_to_bf16_bits(w)
+        del w
     return out
