@@ -1,11 +1,16 @@
-"""AdaS-Attn (AdaSpark adaptive cube-selective attention) on MI355X.
+"""AdaS-Attn (AdaSpark adaptive cube-selective attention) and AdaS-FFN
+(adaptive token-selective FFN) on MI355X.
 
 The computation lives in libadas.so (hand-written HIP for gfx950, C ABI in
-include/adas.h).  This package is its Python binding (``_lib``) plus
-``AdasAttention``, which owns the device buffers of one layer and chains the
-four library calls:
+include/adas.h and include/adas_ffn.h).  This package is its Python binding
+(``_lib``) plus ``AdasAttention``, which owns the device buffers of one layer
+and chains the four library calls:
 
     cube partition (Q, K, V) -> cube mean keys -> Top-p (or Top-K) selection -> attention
+
+and ``AdasFFN``, which chains the two AdaS-FFN calls:
+
+    token selection per cube -> FFN of active tokens + mean compensation
 
 Torch is used for device memory and streams only.
 """
@@ -17,7 +22,8 @@ import torch
 
 from ._lib import (  # noqa: F401
     ADAS_BF16, ADAS_F32, ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT, ADAS_WS_ATTN, ADAS_WS_SELECT,
-    AdasError, Geometry, LIB_PATH,
+    AdasError, FfnGeometry, Geometry, LIB_PATH,
+    adas_ffn_fwd, adas_ffn_select, adas_ffn_workspace_bytes,
     adas_cube_mean_keys, adas_cube_partition, adas_select_topk, adas_select_topp, adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
 )
@@ -27,6 +33,7 @@ __all__ = [
     "adas_select_topp", "adas_select_topk", "adas_sparse_attn_fwd", "adas_workspace_bytes",
     "adas_sel_capacity",
     "adas_version", "load", "LIB_PATH",
+    "FfnGeometry", "AdasFFN", "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
 ]
 
 
@@ -107,3 +114,41 @@ class AdasAttention:
         self.select(q_extra, stream=stream)
         self.attend(q_extra, None, None, stream)
         return self.out_extra
+
+
+class AdasFFN:
+    """Buffers and call sequence for one AdaS-FFN layer on one device.
+
+    Weights are bf16 in the nn.Linear layout (w_gate, w_up [inter][hidden],
+    w_down [hidden][inter]); n_text text tokens go through the FFN densely.
+    """
+
+    def __init__(self, geom: FfnGeometry, p: float, w_gate: torch.Tensor, w_up: torch.Tensor,
+                 w_down: torch.Tensor, n_text: int = 0, device="cuda"):
+        load()
+        self.geom, self.p, self.n_text = geom, float(p), n_text
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        dev = torch.device(device)
+        g = geom
+        i32 = dict(device=dev, dtype=torch.int32)
+        self.act_count = torch.empty((g.n_cubes,), **i32)
+        self.act_off = torch.empty((g.n_cubes + 1,), **i32)
+        self.act_rows = torch.empty((g.N,), **i32)
+        self.act_mask = torch.empty((g.n_cubes, g.mask_words), **i32)
+        self.y = torch.empty((g.N, g.hidden), device=dev, dtype=torch.bfloat16)
+        self.y_text = torch.empty((n_text, g.hidden), device=dev, dtype=torch.bfloat16) if n_text else None
+        ws = adas_ffn_workspace_bytes(g, n_text)
+        self.ws = torch.empty((ws,), device=dev, dtype=torch.uint8)
+
+    def select(self, x: torch.Tensor, stream=None):
+        adas_ffn_select(self.geom, x, self.p, self.act_count, self.act_off, self.act_rows, self.act_mask,
+                        stream)
+
+    def ffn(self, x: torch.Tensor, x_text: Optional[torch.Tensor] = None, stream=None):
+        adas_ffn_fwd(self.geom, x, x_text, self.w_gate, self.w_up, self.w_down, self.act_off,
+                     self.act_rows, self.act_mask, self.y, self.y_text, self.ws, stream)
+
+    def forward(self, x: torch.Tensor, x_text: Optional[torch.Tensor] = None, stream=None):
+        self.select(x, stream)
+        self.ffn(x, x_text, stream)
+        return self.y, self.y_text

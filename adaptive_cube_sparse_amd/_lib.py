@@ -1,4 +1,4 @@
-"""ctypes binding of libadas (include/adas.h).
+"""ctypes binding of libadas (include/adas.h, include/adas_ffn.h).
 
 Argument marshalling only: every function here checks tensor dtypes, devices
 and shapes, turns tensors into raw pointers and calls the C entry point of
@@ -24,11 +24,13 @@ ADAS_WS_SELECT, ADAS_WS_ATTN = 0, 1
 ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT = 0, 1
 ADAS_MAX_HEADS = 128
 ADAS_MAX_CUBES = 4096
+ADAS_FFN_MAX_S = 256
 
 EXPORTS = (
     "adas_cube_partition", "adas_cube_mean_keys", "adas_select_topp", "adas_select_topk",
     "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
     "adas_status_string", "adas_last_error", "adas_version",
+    "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
 )
 
 
@@ -42,6 +44,10 @@ class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "H", "W", "ct", "ch", "cw", "n_q_heads", "n_kv_heads", "head_dim")] + \
                [("head_map", ctypes.POINTER(ctypes.c_int32))]
+
+
+class _FfnGeom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "W", "ct", "ch", "cw", "hidden", "inter")]
 
 
 _lib = None
@@ -58,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     gp = ctypes.POINTER(_Geom)
+    fgp = ctypes.POINTER(_FfnGeom)
+    f64 = ctypes.c_double
     sig = {
         "adas_cube_partition": (i32, [gp, i32, i32, i32, vp, vp, vp, vp]),
         "adas_cube_mean_keys": (i32, [gp, i32, vp, vp, vp]),
@@ -70,6 +78,9 @@ def load() -> ctypes.CDLL:
         "adas_status_string": (ctypes.c_char_p, [i32]),
         "adas_last_error": (ctypes.c_char_p, []),
         "adas_version": (ctypes.c_char_p, []),
+        "adas_ffn_select": (i32, [fgp, vp, f64, vp, vp, vp, vp, vp]),
+        "adas_ffn_fwd": (i32, [fgp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "adas_ffn_workspace_bytes": (sz, [fgp, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -279,3 +290,89 @@ def adas_sel_capacity(geom: Geometry, has_video: bool, n_extra: int) -> int:
 
 def adas_version() -> str:
     return load().adas_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# AdaS-FFN (include/adas_ffn.h)
+# ---------------------------------------------------------------------------
+@dataclass
+class FfnGeometry:
+    """Video grid T x H x W, cube extents (ct, ch, cw), model and FFN widths."""
+    T: int
+    H: int
+    W: int
+    ct: int
+    ch: int
+    cw: int
+    hidden: int
+    inter: int
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def S(self) -> int:
+        return self.ct * self.ch * self.cw
+
+    @property
+    def n_cubes(self) -> int:
+        return self.N // self.S
+
+    @property
+    def mask_words(self) -> int:
+        return (self.S + 31) // 32
+
+    def _c(self):
+        return _FfnGeom(self.T, self.H, self.W, self.ct, self.ch, self.cw, self.hidden, self.inter)
+
+
+def adas_ffn_select(geom: FfnGeometry, x: torch.Tensor, p: float, act_count: torch.Tensor,
+                    act_off: torch.Tensor, act_rows: torch.Tensor, act_mask: torch.Tensor,
+                    stream=None) -> None:
+    """Per-cube Top-p over token L2-norm shares: x [N][hidden] bf16 ->
+    act_count [Nc], act_off [Nc+1], act_rows [N] int32, act_mask [Nc][words]."""
+    lib = load()
+    _shape(x, (geom.N, geom.hidden), "x")
+    _shape(act_count, (geom.n_cubes,), "act_count")
+    _shape(act_off, (geom.n_cubes + 1,), "act_off")
+    _shape(act_rows, (geom.N,), "act_rows")
+    _shape(act_mask, (geom.n_cubes, geom.mask_words), "act_mask")
+    g = geom._c()
+    st = lib.adas_ffn_select(ctypes.byref(g), _ptr(x, torch.bfloat16, "x"), float(p),
+                             _ptr(act_count, torch.int32, "act_count"), _ptr(act_off, torch.int32, "act_off"),
+                             _ptr(act_rows, torch.int32, "act_rows"), _ptr(act_mask, torch.int32, "act_mask"),
+                             _stream(stream))
+    _check(st, "adas_ffn_select")
+
+
+def adas_ffn_fwd(geom: FfnGeometry, x: torch.Tensor, x_text: Optional[torch.Tensor], w_gate: torch.Tensor,
+                 w_up: torch.Tensor, w_down: torch.Tensor, act_off: torch.Tensor, act_rows: torch.Tensor,
+                 act_mask: torch.Tensor, y: torch.Tensor, y_text: Optional[torch.Tensor],
+                 ws: torch.Tensor, stream=None) -> None:
+    """FFN of the active tokens, mean compensation of the skipped ones, dense
+    text tokens; see adas_ffn.h."""
+    lib = load()
+    n_text = 0 if x_text is None else x_text.shape[0]
+    bf = torch.bfloat16
+    _shape(x, (geom.N, geom.hidden), "x")
+    _shape(y, (geom.N, geom.hidden), "y")
+    _shape(w_gate, (geom.inter, geom.hidden), "w_gate")
+    _shape(w_up, (geom.inter, geom.hidden), "w_up")
+    _shape(w_down, (geom.hidden, geom.inter), "w_down")
+    if n_text:
+        _shape(x_text, (n_text, geom.hidden), "x_text")
+        _shape(y_text, (n_text, geom.hidden), "y_text")
+    g = geom._c()
+    st = lib.adas_ffn_fwd(ctypes.byref(g), _ptr(x, bf, "x"), n_text, _ptr(x_text, bf, "x_text"),
+                          _ptr(w_gate, bf, "w_gate"), _ptr(w_up, bf, "w_up"), _ptr(w_down, bf, "w_down"),
+                          _ptr(act_off, torch.int32, "act_off"), _ptr(act_rows, torch.int32, "act_rows"),
+                          _ptr(act_mask, torch.int32, "act_mask"), _ptr(y, bf, "y"), _ptr(y_text, bf, "y_text"),
+                          _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "adas_ffn_fwd")
+
+
+def adas_ffn_workspace_bytes(geom: FfnGeometry, n_text: int) -> int:
+    lib = load()
+    g = geom._c()
+    return int(lib.adas_ffn_workspace_bytes(ctypes.byref(g), int(n_text)))

@@ -9,7 +9,9 @@
 #include <cstring>
 
 #include "adas.h"
+#include "adas_ffn.h"
 #include "common.h"
+#include "ffn.h"
 
 namespace {
 
@@ -272,6 +274,93 @@ int64_t adas_sel_capacity(const adas_geom* geom, int32_t has_video, int32_t n_ex
   adas::HeadGroups hg;
   if (derive(geom, g, hg) != ADAS_OK || n_extra < 0) return -1;
   return capacity_of(g, has_video != 0, n_extra);
+}
+
+// ---------------------------------------------------------------------------
+// AdaS-FFN
+// ---------------------------------------------------------------------------
+static adas_status derive_ffn(const adas_ffn_geom* geom, adas::KGeom& g) {
+  if (geom == nullptr) return fail(ADAS_ERR_NULL, "geom is NULL");
+  const adas_ffn_geom& s = *geom;
+  if (s.T <= 0 || s.H <= 0 || s.W <= 0 || s.ct <= 0 || s.ch <= 0 || s.cw <= 0)
+    return fail(ADAS_ERR_SHAPE, "grid and cube extents must be positive");
+  if (s.T % s.ct || s.H % s.ch || s.W % s.cw)
+    return fail(ADAS_ERR_SHAPE, "cube %dx%dx%d (t,h,w) does not divide grid %dx%dx%d", s.ct, s.ch,
+                s.cw, s.T, s.H, s.W);
+  const long long N = (long long)s.T * s.H * s.W;
+  if (N > (1LL << 28)) return fail(ADAS_ERR_SHAPE, "too many tokens (%lld)", N);
+  const int S = s.ct * s.ch * s.cw;
+  if (S > ADAS_FFN_MAX_S)
+    return fail(ADAS_ERR_SHAPE, "%d tokens per cube exceed the limit %d", S, ADAS_FFN_MAX_S);
+  if (s.hidden <= 0 || s.hidden % 256 || s.hidden > 65536)
+    return fail(ADAS_ERR_SHAPE, "hidden must be a positive multiple of 256 up to 65536 (got %d)", s.hidden);
+  if (s.inter <= 0 || s.inter % 128 || s.inter > 262144)
+    return fail(ADAS_ERR_SHAPE, "inter must be a positive multiple of 128 up to 262144 (got %d)", s.inter);
+  g = adas::KGeom{};
+  g.T = s.T; g.H = s.H; g.W = s.W;
+  g.ct = s.ct; g.ch = s.ch; g.cw = s.cw;
+  g.nT = s.T / s.ct; g.nH = s.H / s.ch; g.nW = s.W / s.cw;
+  g.N = (int)N;
+  g.S = S;
+  g.Nc = g.nT * g.nH * g.nW;
+  return ADAS_OK;
+}
+
+adas_status adas_ffn_select(const adas_ffn_geom* geom, const void* x, double p,
+                            int32_t* act_count, int32_t* act_off, int32_t* act_rows,
+                            uint32_t* act_mask, void* stream) {
+  adas::KGeom g;
+  adas_status st = derive_ffn(geom, g);
+  if (st != ADAS_OK) return st;
+  if (!(p > 0.0 && p <= 1.0)) return fail(ADAS_ERR_VALUE, "p must be in (0, 1] (got %g)", p);
+  if (x == nullptr || act_count == nullptr || act_off == nullptr || act_rows == nullptr ||
+      act_mask == nullptr)
+    return fail(ADAS_ERR_NULL, "x/act_count/act_off/act_rows/act_mask is NULL");
+  return hip_status(adas::launch_ffn_select(g, geom->hidden, x, p, act_count, act_off, act_rows,
+                                            act_mask, (hipStream_t)stream),
+                    "adas_ffn_select launch");
+}
+
+adas_status adas_ffn_fwd(const adas_ffn_geom* geom, const void* x, int32_t n_text,
+                         const void* x_text, const void* w_gate, const void* w_up,
+                         const void* w_down, const int32_t* act_off, const int32_t* act_rows,
+                         const uint32_t* act_mask, void* y, void* y_text, void* ws,
+                         size_t ws_bytes, void* stream) {
+  adas::KGeom g;
+  adas_status st = derive_ffn(geom, g);
+  if (st != ADAS_OK) return st;
+  if (n_text < 0 || n_text > (1 << 24)) return fail(ADAS_ERR_SHAPE, "n_text out of range (%d)", n_text);
+  if (x == nullptr || w_gate == nullptr || w_up == nullptr || w_down == nullptr ||
+      act_off == nullptr || act_rows == nullptr || act_mask == nullptr || y == nullptr)
+    return fail(ADAS_ERR_NULL, "x/weights/selection/y is NULL");
+  if (n_text > 0 && (x_text == nullptr || y_text == nullptr))
+    return fail(ADAS_ERR_NULL, "x_text/y_text is NULL");
+  const size_t need = adas::ffn_workspace_bytes(g, geom->hidden, geom->inter, n_text);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  adas::FfnArgs f;
+  f.g = g;
+  f.hidden = geom->hidden;
+  f.inter = geom->inter;
+  f.n_text = n_text;
+  f.x = x;
+  f.x_text = x_text;
+  f.w_gate = w_gate;
+  f.w_up = w_up;
+  f.w_down = w_down;
+  f.act_off = act_off;
+  f.act_rows = act_rows;
+  f.act_mask = act_mask;
+  f.y = y;
+  f.y_text = y_text;
+  f.ws = ws;
+  return hip_status(adas::launch_ffn(f, (hipStream_t)stream), "adas_ffn_fwd launch");
+}
+
+size_t adas_ffn_workspace_bytes(const adas_ffn_geom* geom, int32_t n_text) {
+  adas::KGeom g;
+  if (derive_ffn(geom, g) != ADAS_OK || n_text < 0) return 0;
+  return adas::ffn_workspace_bytes(g, geom->hidden, geom->inter, n_text);
 }
 
 const char* adas_status_string(adas_status s) {

@@ -17,6 +17,12 @@ The printed JSON line reports:
               peak; "traffic" is the counter-measured HBM bytes per call when
               profiles/attn_traffic.json matches the current sources;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+
+With an AdaS-FFN workload (--config ffn3b, ffn7b, ffn_hour, ffn_tiny) a step
+is instead one AdaS-FFN layer: per-cube token selection, then the FFN of the
+active and text tokens plus mean compensation of the skipped ones; "value" is
+6 * hidden * inter * (active + text tokens) FLOPs per step time, and the
+roofline covers the adas_ffn_fwd call (its two GEMMs and the combine pass).
 """
 from __future__ import annotations
 
@@ -44,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD,
-                    help="workload name (tiny, qwen3b, qwen7b_p05/p07/p09, hour, decode)")
+                    help="workload name (tiny, qwen3b, qwen7b_p05/p07/p09, hour, decode; AdaS-FFN: "
+                         "ffn_tiny, ffn3b, ffn7b, ffn_hour)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -195,6 +202,105 @@ def cpu_baseline(wl, data, budget_s: float, topk: int = 0):
             "host_threads_available": len(os.sched_getaffinity(0))}
 
 
+FFN_METRIC = "AdaS-FFN effective TFLOP/s (active + text tokens) and % of MI355X bf16 peak"
+
+
+def ffn_cpu_baseline(wl, data, budget_s: float):
+    """Time the CPU oracle (float64 NumPy, one BLAS thread) on whole cubes of
+    the workload, drawn at random until the budget is spent."""
+    from threadpoolctl import threadpool_limits
+    from oracle import adas_oracle as O
+    from oracle import ffn_oracle as F
+    rng = np.random.default_rng(123)
+    g = O.Geometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw)
+    w64 = (O.to_f64(data["w_gate"]), O.to_f64(data["w_up"]), O.to_f64(data["w_down"]))
+    flops, cubes, t = 0.0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while t < budget_s:
+            c = int(rng.integers(g.n_cubes))
+            t1 = time.perf_counter()
+            (toks, act, _), = F.adas_ffn_cubes(data["x"], g, wl.p, None, None, None, cubes=[c],
+                                               weights64=w64).values()
+            t += time.perf_counter() - t1
+            flops += 6.0 * wl.hidden * wl.inter * len(act)
+            cubes += 1
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{cubes} random cubes of {wl.name} (norms, Top-p, SwiGLU FFN of the active "
+                      f"tokens, mean compensation; float64 NumPy, 1 BLAS thread) in {t:.1f} s",
+            "host_threads_available": len(os.sched_getaffinity(0))}
+
+
+def ffn_main(args):
+    import torch
+    import workloads
+    from adaptive_cube_sparse_amd import AdasFFN, FfnGeometry
+
+    wl = workloads.get_ffn(args.config)
+    dev = torch.device("cuda:0")
+    data = workloads.generate_ffn(wl)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    geom = FfnGeometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw, wl.hidden, wl.inter)
+    layer = AdasFFN(geom, wl.p, up(data["w_gate"]), up(data["w_up"]), up(data["w_down"]),
+                    n_text=wl.n_text, device=dev)
+    x = up(data["x"])
+    xt = up(data["x_text"]) if wl.n_text else None
+    stream = torch.cuda.current_stream()
+    ev = {"select": [], "ffn": []}
+
+    def step(record):
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+        e0 = mark() if record else None
+        layer.select(x)
+        e1 = mark() if record else None
+        layer.ffn(x, xt)
+        e2 = mark() if record else None
+        if record:
+            ev["select"].append((e0, e1))
+            ev["ffn"].append((e1, e2))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in p])) for n, p in ev.items()}
+    m_active = int(layer.act_off[-1].item())
+    rows = m_active + wl.n_text
+    flops = 6.0 * wl.hidden * wl.inter * rows
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (k_ms["ffn"] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "kernels": ["adas::k_ffn_gemm<true>", "adas::k_ffn_gemm<false>", "adas::k_ffn_combine"],
+            "launch_ms": k_ms["ffn"]}
+    cpu = None if args.no_cpu_baseline else ffn_cpu_baseline(wl, data, args.cpu_seconds)
+    out = {
+        "metric": FFN_METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "grid": [wl.T, wl.H, wl.W], "cube_thw": [wl.ct, wl.ch, wl.cw],
+                   "hidden": wl.hidden, "inter": wl.inter, "p": wl.p, "text_tokens": wl.n_text,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_ms": k_ms,
+        "active_tokens": m_active,
+        "keep_ratio": m_active / wl.n_tokens,
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -212,6 +318,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 3}))
         return
     import workloads
+    if args.config in workloads.FFN_WORKLOADS:
+        return ffn_main(args)
     from adaptive_cube_sparse_amd import AdasAttention, Geometry
 
     wl = workloads.get(args.config)

@@ -1,5 +1,5 @@
 """CPU checks of the C ABI: the library loads, exports every symbol declared
-in include/adas.h, sizes buffers by the closed forms, and rejects invalid
+in include/adas.h and include/adas_ffn.h, sizes buffers by the closed forms, and rejects invalid
 arguments on the host before any launch (no GPU needed; no compute call)."""
 import ctypes
 import os
@@ -10,15 +10,17 @@ import pytest
 from tests.conftest import ROOT
 
 LIB = os.path.join(ROOT, "adaptive_cube_sparse_amd", "libadas.so")
-HEADER = os.path.join(ROOT, "include", "adas.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("adas.h", "adas_ffn.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libadas.so not built")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(adas_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(adas_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -162,3 +164,36 @@ def test_attention_and_partition_reject_invalid_arguments_on_host():
     need = lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_ATTN, 0, 2)
     assert need > 0
     assert attn(q_cube=None, out=None, n_extra=2, q_extra=FAKE, out_x=FAKE) == L.ADAS_ERR_WORKSPACE
+
+
+def _ffn_geom(**kw):
+    import adaptive_cube_sparse_amd._lib as L
+    base = dict(T=4, H=8, W=8, ct=2, ch=4, cw=4, hidden=256, inter=384)
+    base.update(kw)
+    return L._FfnGeom(**base)
+
+
+def test_ffn_workspace_closed_form_and_host_validation():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _ffn_geom()
+    rows = (256 + 5 + 255) // 256 * 256
+    assert lib.adas_ffn_workspace_bytes(ctypes.byref(g), 5) == rows * 384 * 2 + rows * 256 * 4 + 256
+    FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails on the host
+    def sel(p=0.7, **kw):
+        gg = _ffn_geom(**kw)
+        return lib.adas_ffn_select(ctypes.byref(gg), FAKE, p, FAKE, FAKE, FAKE, FAKE, None)
+    for bad in (0.0, -0.1, 1.5, float("nan")):
+        assert sel(bad) == L.ADAS_ERR_VALUE
+    assert sel(hidden=200) == L.ADAS_ERR_SHAPE
+    assert sel(ct=3) == L.ADAS_ERR_SHAPE
+    assert sel(T=8, H=8, W=8, ct=8, ch=8, cw=8) == L.ADAS_ERR_SHAPE  # S = 512 > ADAS_FFN_MAX_S
+    assert lib.adas_ffn_select(ctypes.byref(g), None, 0.7, FAKE, FAKE, FAKE, FAKE, None) == L.ADAS_ERR_NULL
+    def fwd(ws_bytes, inter=384, n_text=0, x_text=None):
+        gg = _ffn_geom(inter=inter)
+        return lib.adas_ffn_fwd(ctypes.byref(gg), FAKE, n_text, x_text, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, ws_bytes, None)
+    need = lib.adas_ffn_workspace_bytes(ctypes.byref(g), 0)
+    assert fwd(need - 1) == L.ADAS_ERR_WORKSPACE
+    assert fwd(need, inter=320) == L.ADAS_ERR_SHAPE
+    assert fwd(need, n_text=3) == L.ADAS_ERR_NULL
