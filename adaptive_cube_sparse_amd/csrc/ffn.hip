@@ -228,9 +228,10 @@ __global__ __launch_bounds__(GNT) void k_ffn_gemm(FfnGemmArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // fragments of k-step ks+1 are read while the MFMAs of k-step ks run; the
-  // scheduling barriers keep the compiler from hoisting every read of the
-  // stage (which would not fit beside the 128 accumulator registers)
+  // Fragments of k-step ks+1 are read while the MFMAs of k-step ks run: the
+  // scheduling group barriers interleave one fragment read after each of the
+  // first six MFMAs, so the reads are under way long before their data is
+  // needed and the only wait on LDS is at the first k-step of a stage.
   auto compute = [&](auto bufc) __attribute__((always_inline)) {
     const uint8_t* sa = decltype(bufc)::value ? sA1 : sA0;
     const uint8_t* sb = decltype(bufc)::value ? sB1 : sB0;
@@ -244,15 +245,23 @@ __global__ __launch_bounds__(GNT) void k_ffn_gemm(FfnGemmArgs a) {
         bv[set][j] = __builtin_bit_cast(gbf16x8, *reinterpret_cast<const uint4*>(sb + boff[j] + koff[ks]));
     };
     load(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][i], bv[ks & 1][j], acc[i][j], 0, 0, 0);
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
