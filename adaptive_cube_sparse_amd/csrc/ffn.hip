@@ -232,7 +232,7 @@ __global__ __launch_bounds__(GNT) void k_ffn_gemm(FfnGemmArgs a) {
   // scheduling group barriers interleave one fragment read after each of the
   // first six MFMAs, so the reads are under way long before their data is
   // needed and the only wait on LDS is at the first k-step of a stage.
-  auto compute = [&](auto bufc) __attribute__((always_inline)) {
+  auto compute = [&](auto bufc, auto nextc, int k_next) __attribute__((always_inline)) {
     const uint8_t* sa = decltype(bufc)::value ? sA1 : sA0;
     const uint8_t* sb = decltype(bufc)::value ? sB1 : sB0;
     gbf16x8 av[2][2], bv[2][4];
@@ -249,12 +249,24 @@ __global__ __launch_bounds__(GNT) void k_ffn_gemm(FfnGemmArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
+      if (ks == 0) issue(k_next, nextc);  // the next stage's loads go out under the first MFMAs
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][i], bv[ks & 1][j], acc[i][j], 0, 0, 0);
-      if (ks + 1 < 4) {
+      if (ks == 0) {
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global -> LDS load
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      } else if (ks + 1 < 4) {
 #pragma unroll
         for (int r = 0; r < 6; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -267,21 +279,22 @@ __global__ __launch_bounds__(GNT) void k_ffn_gemm(FfnGemmArgs a) {
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  // stage s lives in buffer s % 2; the barrier before stage s also tells every
+  // Stage s lives in buffer s % 2; the barrier before stage s also tells every
   // wave that stage s-1 (the other buffer) is no longer read, so stage s+1
-  // may land there.  The host guarantees an even number of stages.
+  // may land there; its loads are issued inside the first k-step of stage s.
+  // Past the last stage the loads repeat it (in bounds, never read), so every
+  // step has the same shape.  The host guarantees an even number of stages.
   const int nst = a.K / GBK;
   issue(0, C0{});
   for (int s = 0; s < nst; s += 2) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage s
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    issue((s + 1) * GBK, C1{});
-    compute(C0{});
+    compute(C0{}, C1{}, (s + 1) * GBK);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (s + 2 < nst) issue((s + 2) * GBK, C0{});
-    compute(C1{});
+    compute(C1{}, C0{}, min(s + 2, nst - 1) * GBK);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated loads land before LDS is reused
 
   // accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32
   if constexpr (GU) {
