@@ -18,9 +18,10 @@ typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 typedef float gf32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
-// selection: one workgroup (256 threads) per cube
+// selection: one workgroup (1024 threads, one wave per token at a time) per cube
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_ffn_select(KGeom g, int hidden, const uint16_t* __restrict__ x,
+constexpr int FSEL_T = 1024;
+__global__ __launch_bounds__(FSEL_T) void k_ffn_select(KGeom g, int hidden, const uint16_t* __restrict__ x,
                                                     double p, int32_t* __restrict__ act_count,
                                                     uint32_t* __restrict__ act_mask, int mw) {
   __shared__ double s_norm[ADAS_FFN_MAX_S];
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void k_ffn_select(KGeom g, int hidden, const u
 
   // squared L2 norm of token r: bf16 values widened to float64, whose
   // products are exact; one wave per token, float64 butterfly at the end
-  for (int r = wave; r < S; r += 4) {
+  for (int r = wave; r < S; r += FSEL_T / 64) {
     const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)raster_of(g, c, r) * hidden);
     double acc = 0.0;
     for (int v = lane; v < nvec; v += 64) {
@@ -342,8 +343,9 @@ __global__ __launch_bounds__(GNT) void k_ffn_gemm(FfnGemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// mean compensation and residual: one workgroup per cube, then one per 16
-// text rows.  Columns go 4 at a time (float4 of F, 8 bytes of bf16).
+// mean compensation and residual.  Block (b, chunk) covers 1024 columns
+// (256 threads x 4) of cube b, or of 16 text rows when b >= Nc; columns go 4
+// at a time (float4 of F, 8 bytes of bf16 x and y).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_ffn_combine(KGeom g, int hidden, const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ x_text, int n_text,
@@ -352,6 +354,8 @@ __global__ __launch_bounds__(256) void k_ffn_combine(KGeom g, int hidden, const 
                                                      const uint32_t* __restrict__ act_mask, int mw,
                                                      uint16_t* __restrict__ y, uint16_t* __restrict__ y_text) {
   const int nv = hidden >> 2;
+  const int v = blockIdx.y * 256 + threadIdx.x;
+  if (v >= nv) return;
   const float4* F4 = reinterpret_cast<const float4*>(F);
   auto add_store = [&](const uint16_t* xs, uint16_t* ys, float4 f) __attribute__((always_inline)) {
     const uint2 xv = *reinterpret_cast<const uint2*>(xs);
@@ -367,17 +371,33 @@ __global__ __launch_bounds__(256) void k_ffn_combine(KGeom g, int hidden, const 
     const int c = b;
     const int beg = act_off[c], cnt = act_off[c + 1] - beg;
     const uint32_t* mk = act_mask + (size_t)c * mw;
-    for (int v = threadIdx.x; v < nv; v += 256) {
-      float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int j = 0; j < cnt; ++j) {
-        const float4 f = F4[(size_t)(beg + j) * nv + v];
-        m.x += f.x; m.y += f.y; m.z += f.z; m.w += f.w;
+    // mean over the active rows, four partial sums for independent loads
+    float4 p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 f = F4[(size_t)(beg + j + u) * nv + v];
+        p[u].x += f.x; p[u].y += f.y; p[u].z += f.z; p[u].w += f.w;
       }
-      const float inv = 1.0f / (float)cnt;
-      m.x *= inv; m.y *= inv; m.z *= inv; m.w *= inv;
-      int slot = 0;
-      for (int r = 0; r < g.S; ++r) {
-        const bool act = (mk[r >> 5] >> (r & 31)) & 1u;
+    }
+    for (; j < cnt; ++j) {
+      const float4 f = F4[(size_t)(beg + j) * nv + v];
+      p[0].x += f.x; p[0].y += f.y; p[0].z += f.z; p[0].w += f.w;
+    }
+    const float inv = 1.0f / (float)cnt;
+    const float4 m = make_float4(((p[0].x + p[1].x) + (p[2].x + p[3].x)) * inv,
+                                 ((p[0].y + p[1].y) + (p[2].y + p[3].y)) * inv,
+                                 ((p[0].z + p[1].z) + (p[2].z + p[3].z)) * inv,
+                                 ((p[0].w + p[1].w) + (p[2].w + p[3].w)) * inv);
+    int slot = 0;
+    for (int r0 = 0; r0 < g.S; r0 += 32) {
+      const uint32_t w = mk[r0 >> 5];
+#pragma unroll 4
+      for (int r = r0; r < min(r0 + 32, g.S); ++r) {
+        const bool act = (w >> (r & 31)) & 1u;
         const size_t n = (size_t)raster_of(g, c, r);
         const float4 f = act ? F4[(size_t)(beg + slot) * nv + v] : m;
         slot += act;
@@ -388,9 +408,8 @@ __global__ __launch_bounds__(256) void k_ffn_combine(KGeom g, int hidden, const 
     const int Mv = act_off[g.Nc];
     const int t0 = (b - g.Nc) * 16;
     for (int t = t0; t < min(t0 + 16, n_text); ++t)
-      for (int v = threadIdx.x; v < nv; v += 256)
-        add_store(x_text + (size_t)t * hidden + 4 * v, y_text + (size_t)t * hidden + 4 * v,
-                  F4[(size_t)(Mv + t) * nv + v]);
+      add_store(x_text + (size_t)t * hidden + 4 * v, y_text + (size_t)t * hidden + 4 * v,
+                F4[(size_t)(Mv + t) * nv + v]);
   }
 }
 
@@ -411,7 +430,7 @@ size_t ffn_workspace_bytes(const KGeom& g, int hidden, int inter, int n_text) {
 hipError_t launch_ffn_select(const KGeom& g, int hidden, const void* x, double p, int32_t* act_count,
                              int32_t* act_off, int32_t* act_rows, uint32_t* act_mask, hipStream_t s) {
   const int mw = ffn_mask_words(g.S);
-  hipLaunchKernelGGL(k_ffn_select, dim3(g.Nc), dim3(256), 0, s, g, hidden,
+  hipLaunchKernelGGL(k_ffn_select, dim3(g.Nc), dim3(FSEL_T), 0, s, g, hidden,
                      static_cast<const uint16_t*>(x), p, act_count, act_mask, mw);
   hipLaunchKernelGGL(k_ffn_emit, dim3(g.Nc), dim3(256), 0, s, g, (const int32_t*)act_count,
                      (const uint32_t*)act_mask, mw, act_off, act_rows);
@@ -455,7 +474,8 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t s) {
   hipLaunchKernelGGL(k_ffn_gemm<false>, dim3(grid_dn), dim3(GNT), 0, s, dn);
 
   const int mw = ffn_mask_words(g.S);
-  hipLaunchKernelGGL(k_ffn_combine, dim3(g.Nc + (f.n_text + 15) / 16), dim3(256), 0, s, g, f.hidden,
+  hipLaunchKernelGGL(k_ffn_combine, dim3(g.Nc + (f.n_text + 15) / 16, (f.hidden / 4 + 255) / 256), dim3(256), 0, s,
+                     g, f.hidden,
                      static_cast<const uint16_t*>(f.x), static_cast<const uint16_t*>(f.x_text), f.n_text,
                      (const float*)F, f.act_off, f.act_mask, mw, static_cast<uint16_t*>(f.y),
                      static_cast<uint16_t*>(f.y_text));
