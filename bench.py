@@ -97,6 +97,31 @@ def attention_kernels(wl, n_extra: int) -> list:
     return ks
 
 
+FFN_SOURCES = ("ffn.hip", "ffn.h", "common.h")
+
+
+def source_hash_of(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "adaptive_cube_sparse_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def ffn_traffic_entry(workload: str):
+    """HBM bytes of one adas_ffn_fwd call from rocprofv3 counters, if the
+    committed measurement is for the current FFN sources."""
+    path = os.path.join(ROOT, "profiles", "ffn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except Exception:
+        return None
+    if not rec or rec.get("ffn_sources_sha256_16") != source_hash_of(FFN_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def traffic_entry(workload: str):
     """HBM traffic of the attention kernel measured with rocprofv3 counters,
     if the committed measurement is for the current kernel source."""
@@ -279,7 +304,7 @@ def ffn_main(args):
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (k_ms["ffn"] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": ffn_traffic_entry(wl.name),
             "algorithmic_flops_per_launch": flops,
             "kernels": ["adas::k_ffn_gemm<true>", "adas::k_ffn_gemm<false>", "adas::k_ffn_combine"],
             "launch_ms": k_ms["ffn"]}
