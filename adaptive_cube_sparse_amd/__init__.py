@@ -8,9 +8,12 @@ and chains the four library calls:
 
     cube partition (Q, K, V) -> cube mean keys -> Top-p (or Top-K) selection -> attention
 
-and ``AdasFFN``, which chains the two AdaS-FFN calls:
+``AdasFFN``, which chains the two AdaS-FFN calls:
 
     token selection per cube -> FFN of active tokens + mean compensation
+
+and ``StreamingCache``, a video KV cache that grows frame by frame while
+decode steps read its completed cubes.
 
 Torch is used for device memory and streams only.
 """
@@ -23,7 +26,7 @@ import torch
 from ._lib import (  # noqa: F401
     ADAS_BF16, ADAS_F32, ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT, ADAS_WS_ATTN, ADAS_WS_SELECT,
     AdasError, FfnGeometry, Geometry, LIB_PATH,
-    adas_ffn_fwd, adas_ffn_select, adas_ffn_workspace_bytes,
+    adas_ffn_fwd, adas_ffn_select, adas_ffn_workspace_bytes, adas_cache_append, adas_cache_sum_bytes,
     adas_cube_mean_keys, adas_cube_partition, adas_select_topk, adas_select_topp, adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
 )
@@ -34,6 +37,7 @@ __all__ = [
     "adas_sel_capacity",
     "adas_version", "load", "LIB_PATH",
     "FfnGeometry", "AdasFFN", "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
+    "adas_cache_append", "adas_cache_sum_bytes", "StreamingCache",
 ]
 
 
@@ -152,3 +156,68 @@ class AdasFFN:
         self.select(x, stream)
         self.ffn(x, x_text, stream)
         return self.y, self.y_text
+
+
+class StreamingCache:
+    """A cube-layout video KV cache allocated for `geom.T` frames (or
+    `geom.cache_T`) and filled as frames arrive (``append``).  Decode steps
+    (``decode``) select among and attend to the cubes of the completed
+    temporal blocks."""
+
+    def __init__(self, geom: Geometry, p: float, device="cuda"):
+        load()
+        self.cap = geom.cache_T or geom.T
+        self.geom = Geometry(self.cap, geom.H, geom.W, geom.ct, geom.ch, geom.cw, geom.n_q_heads,
+                             geom.n_kv_heads, geom.head_dim, geom.head_map, self.cap)
+        self.p = float(p)
+        g = self.geom
+        dev = torch.device(device)
+        self.device = dev
+        bf = dict(device=dev, dtype=torch.bfloat16)
+        self.k_cache = torch.empty((g.n_kv_heads, g.NS, g.head_dim), **bf)
+        self.v_cache = torch.empty((g.n_kv_heads, g.NS // g.S, g.head_dim, g.S), **bf)
+        self.kbar = torch.empty((g.n_kv_heads, g.NS // g.S, g.head_dim), device=dev, dtype=torch.float32)
+        self.ksum = torch.empty((adas_cache_sum_bytes(g),), device=dev, dtype=torch.uint8)
+        self.frames = 0
+        self._bufs = {}
+
+    @property
+    def complete_frames(self) -> int:
+        return self.frames // self.geom.ct * self.geom.ct
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        """k_new, v_new [n*H*W][Hkv][d] bf16: the next n frames."""
+        n = k_new.shape[0] // (self.geom.H * self.geom.W)
+        adas_cache_append(self.geom, self.frames, k_new, v_new, self.k_cache, self.v_cache, self.kbar,
+                          self.ksum, stream)
+        self.frames += n
+
+    def decode_geometry(self) -> Geometry:
+        g = self.geom
+        return Geometry(self.complete_frames, g.H, g.W, g.ct, g.ch, g.cw, g.n_q_heads, g.n_kv_heads,
+                        g.head_dim, g.head_map, self.cap)
+
+    def decode(self, q_extra: torch.Tensor, stream=None):
+        """One decode step for q_extra [n][Hq][d] over the completed cubes;
+        returns (out [n][Hq][d], sel_count, sel_idx)."""
+        if self.complete_frames == 0:
+            raise ValueError("no complete temporal block in the cache yet")
+        g = self.decode_geometry()
+        n = q_extra.shape[0]
+        key = (g.T, n)
+        if key not in self._bufs:
+            cap = adas_sel_capacity(g, False, n)
+            ws_s = adas_workspace_bytes(g, torch.bfloat16, ADAS_WS_SELECT, False, n)
+            ws_a = adas_workspace_bytes(g, torch.bfloat16, ADAS_WS_ATTN, False, n)
+            dev = self.device
+            self._bufs[key] = (
+                torch.empty((g.n_q_heads, n), device=dev, dtype=torch.int32),
+                torch.empty((cap,), device=dev, dtype=torch.int32),
+                torch.empty((max(ws_s, 1),), device=dev, dtype=torch.uint8),
+                torch.empty((max(ws_a, 1),), device=dev, dtype=torch.uint8),
+                torch.empty((n, g.n_q_heads, g.head_dim), device=dev, dtype=torch.bfloat16))
+        cnt, idx, ws_s, ws_a, out = self._bufs[key]
+        adas_select_topp(g, None, q_extra, self.kbar, self.p, cnt, idx, ws_s, stream)
+        adas_sparse_attn_fwd(g, None, self.k_cache, self.v_cache, q_extra, None, None, cnt, idx, None, out,
+                             ws_a, stream)
+        return out, cnt, idx

@@ -31,6 +31,7 @@ EXPORTS = (
     "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
     "adas_status_string", "adas_last_error", "adas_version",
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
+    "adas_cache_append", "adas_cache_sum_bytes",
 )
 
 
@@ -43,7 +44,7 @@ class AdasError(RuntimeError):
 class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "H", "W", "ct", "ch", "cw", "n_q_heads", "n_kv_heads", "head_dim")] + \
-               [("head_map", ctypes.POINTER(ctypes.c_int32))]
+               [("head_map", ctypes.POINTER(ctypes.c_int32)), ("cache_T", ctypes.c_int32)]
 
 
 class _FfnGeom(ctypes.Structure):
@@ -81,6 +82,8 @@ def load() -> ctypes.CDLL:
         "adas_ffn_select": (i32, [fgp, vp, f64, vp, vp, vp, vp, vp]),
         "adas_ffn_fwd": (i32, [fgp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "adas_ffn_workspace_bytes": (sz, [fgp, i32]),
+        "adas_cache_append": (i32, [gp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "adas_cache_sum_bytes": (sz, [gp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -106,10 +109,16 @@ class Geometry:
     n_kv_heads: int
     head_dim: int
     head_map: Optional[Sequence[int]] = None
+    cache_T: int = 0   # frames per head allocated in cube-layout buffers (0: T)
 
     @property
     def N(self) -> int:
         return self.T * self.H * self.W
+
+    @property
+    def NS(self) -> int:
+        """Tokens per head of a cube-layout buffer."""
+        return (self.cache_T or self.T) * self.H * self.W
 
     @property
     def S(self) -> int:
@@ -122,6 +131,7 @@ class Geometry:
     def _c(self):
         g = _Geom(self.T, self.H, self.W, self.ct, self.ch, self.cw, self.n_q_heads,
                   self.n_kv_heads, self.head_dim)
+        g.cache_T = self.cache_T
         keep = None
         if self.head_map is not None:
             keep = (ctypes.c_int32 * len(self.head_map))(*[int(x) for x in self.head_map])
@@ -181,9 +191,9 @@ def adas_cube_partition(geom: Geometry, x_raster: torch.Tensor, x_cube: torch.Te
     lib = load()
     N, nh, d = x_raster.shape
     if layout == ADAS_LAYOUT_VT:
-        _shape(x_cube, (nh, geom.n_cubes, d, geom.S), "x_cube")
+        _shape(x_cube, (nh, geom.NS // geom.S, d, geom.S), "x_cube")
     else:
-        _shape(x_cube, (nh, N, d), "x_cube")
+        _shape(x_cube, (nh, geom.NS, d), "x_cube")
     _shape(perm, (N,), "perm")
     g, keep = geom._c()
     st = lib.adas_cube_partition(ctypes.byref(g), _dtype_code(x_raster), nh, int(layout),
@@ -197,8 +207,8 @@ def adas_cube_mean_keys(geom: Geometry, k_cube: torch.Tensor, kbar: torch.Tensor
                         stream=None) -> None:
     """k_cube [Hkv][N][d] -> kbar [Hkv][Nc][d] float32."""
     lib = load()
-    _shape(k_cube, (geom.n_kv_heads, geom.N, geom.head_dim), "k_cube")
-    _shape(kbar, (geom.n_kv_heads, geom.n_cubes, geom.head_dim), "kbar")
+    _shape(k_cube, (geom.n_kv_heads, geom.NS, geom.head_dim), "k_cube")
+    _shape(kbar, (geom.n_kv_heads, geom.NS // geom.S, geom.head_dim), "kbar")
     g, keep = geom._c()
     st = lib.adas_cube_mean_keys(ctypes.byref(g), _dtype_code(k_cube), _ptr(k_cube, name="k_cube"),
                                  _ptr(kbar, torch.float32, "kbar"), _stream(stream))
@@ -209,7 +219,7 @@ def _select(fn, name, geom, q_cube, q_extra, kbar, arg, sel_count, sel_idx, ws, 
     lib = load()
     ref = q_cube if q_cube is not None else q_extra
     n_extra = 0 if q_extra is None else q_extra.shape[0]
-    _shape(q_cube, (geom.n_q_heads, geom.N, geom.head_dim), "q_cube")
+    _shape(q_cube, (geom.n_q_heads, geom.NS, geom.head_dim), "q_cube")
     if q_extra is not None:
         _shape(q_extra, (n_extra, geom.n_q_heads, geom.head_dim), "q_extra")
     rows = (geom.N if q_cube is not None else 0) + n_extra
@@ -252,9 +262,9 @@ def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text
     n_extra = 0 if q_extra is None else q_extra.shape[0]
     n_text_kv = 0 if k_text is None else k_text.shape[0]
     Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
-    _shape(q_cube, (Hq, geom.N, d), "q_cube")
-    _shape(k_cube, (Hkv, geom.N, d), "k_cube")
-    _shape(v_cube, (Hkv, geom.n_cubes, d, geom.S), "v_cube")  # ADAS_LAYOUT_VT
+    _shape(q_cube, (Hq, geom.NS, d), "q_cube")
+    _shape(k_cube, (Hkv, geom.NS, d), "k_cube")
+    _shape(v_cube, (Hkv, geom.NS // geom.S, d, geom.S), "v_cube")  # ADAS_LAYOUT_VT
     _shape(out_raster, (geom.N, Hq, d), "out_raster")
     if n_extra:
         _shape(q_extra, (n_extra, Hq, d), "q_extra")
@@ -272,6 +282,44 @@ def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text
         _ptr(out_raster, dt, "out_raster"), _ptr(out_extra, dt, "out_extra"),
         _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "adas_sparse_attn_fwd")
+
+
+def adas_cache_append(geom: Geometry, t0: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, kbar: torch.Tensor,
+                      ksum: torch.Tensor, stream=None) -> None:
+    """Append frames t0 .. t0 + n - 1 (k_new, v_new [n*H*W][Hkv][d], bf16) to a
+    cube-layout KV cache sized for `geom` (T or cache_T frames); mean keys of
+    completed cubes go to kbar.  ksum: adas_cache_sum_bytes() bytes kept
+    between calls."""
+    lib = load()
+    hw = geom.H * geom.W
+    if k_new.shape[0] % hw:
+        raise ValueError("k_new must hold whole frames")
+    n = k_new.shape[0] // hw
+    Hkv, d = geom.n_kv_heads, geom.head_dim
+    cap = geom.cache_T or geom.T
+    ns = cap * hw
+    _shape(k_new, (n * hw, Hkv, d), "k_new")
+    _shape(v_new, (n * hw, Hkv, d), "v_new")
+    _shape(k_cache, (Hkv, ns, d), "k_cache")
+    _shape(v_cache, (Hkv, ns // geom.S, d, geom.S), "v_cache")
+    _shape(kbar, (Hkv, ns // geom.S, d), "kbar")
+    g, keep = geom._c()
+    need = lib.adas_cache_sum_bytes(ctypes.byref(g))
+    if ksum.numel() * ksum.element_size() < need:
+        raise ValueError(f"ksum holds {ksum.numel() * ksum.element_size()} bytes, needs {need}")
+    bf = torch.bfloat16
+    st = lib.adas_cache_append(ctypes.byref(g), ADAS_BF16, int(t0), n, _ptr(k_new, bf, "k_new"),
+                               _ptr(v_new, bf, "v_new"), _ptr(k_cache, bf, "k_cache"),
+                               _ptr(v_cache, bf, "v_cache"), _ptr(kbar, torch.float32, "kbar"),
+                               _ptr(ksum, name="ksum"), _stream(stream))
+    _check(st, "adas_cache_append")
+
+
+def adas_cache_sum_bytes(geom: Geometry) -> int:
+    lib = load()
+    g, keep = geom._c()
+    return int(lib.adas_cache_sum_bytes(ctypes.byref(g)))
 
 
 def adas_workspace_bytes(geom: Geometry, dtype: torch.dtype, kind: int, has_video: bool,

@@ -55,6 +55,12 @@ adas_status derive(const adas_geom* geom, adas::KGeom& g, adas::HeadGroups& hg) 
   g.Hq = s.n_q_heads;
   g.Hkv = s.n_kv_heads;
   g.D = s.head_dim;
+  if (s.cache_T != 0 && (s.cache_T < s.T || s.cache_T % s.ct))
+    return fail(ADAS_ERR_SHAPE, "cache_T (%d) must be 0 or a multiple of ct (%d) that is >= T (%d)", s.cache_T,
+                s.ct, s.T);
+  const long long NS = (long long)(s.cache_T ? s.cache_T : s.T) * s.H * s.W;
+  if (NS > (1LL << 30)) return fail(ADAS_ERR_SHAPE, "cache too large (%lld tokens)", NS);
+  g.NS = (int)NS;
   int map[ADAS_MAX_HEADS];
   if (s.head_map == nullptr) {
     if (s.n_q_heads % s.n_kv_heads)
@@ -252,6 +258,37 @@ adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const 
   adas::bind_attention_workspace(a, dtype, ws);
   return hip_status(adas::launch_attention(a, dtype, (hipStream_t)stream),
                     "adas_sparse_attn_fwd launch");
+}
+
+adas_status adas_cache_append(const adas_geom* geom, adas_dtype dtype, int32_t t0, int32_t n_frames,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              float* kbar, double* ksum, void* stream) {
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  adas_status st = derive(geom, g, hg);
+  if (st != ADAS_OK) return st;
+  if (dtype != ADAS_BF16) return fail(ADAS_ERR_DTYPE, "adas_cache_append supports bf16 only");
+  const int cap = geom->cache_T ? geom->cache_T : geom->T;
+  if (t0 < 0 || n_frames <= 0 || (long long)t0 + n_frames > cap)
+    return fail(ADAS_ERR_SHAPE, "frames [%d, %d) outside the cache of %d frames", t0, t0 + n_frames, cap);
+  if (k_new == nullptr || v_new == nullptr || k_cache == nullptr || v_cache == nullptr || kbar == nullptr ||
+      ksum == nullptr)
+    return fail(ADAS_ERR_NULL, "k_new/v_new/k_cache/v_cache/kbar/ksum is NULL");
+  // kernels index the whole cache: its grid is the capacity
+  g.T = cap;
+  g.nT = cap / g.ct;
+  g.N = g.NS;
+  g.Nc = g.NS / g.S;
+  return hip_status(adas::launch_cache_append(g, t0, t0 + n_frames, k_new, v_new, k_cache, v_cache, kbar, ksum,
+                                              (hipStream_t)stream),
+                    "adas_cache_append launch");
+}
+
+size_t adas_cache_sum_bytes(const adas_geom* geom) {
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  if (derive(geom, g, hg) != ADAS_OK) return 0;
+  return (size_t)g.Hkv * g.nH * g.nW * g.D * sizeof(double);
 }
 
 size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kind kind,

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_video_ro
     hq = row_id / g.N;
     pos = row_id - hq * g.N;
     own = pos / g.S;
-    q = (const float*)a.q_cube + ((size_t)hq * g.N + pos) * D;
+    q = (const float*)a.q_cube + ((size_t)hq * g.NS + pos) * D;
     off = video_list_offset(a.capv, hq, g.S, own, pos - own * g.S);
     row_index = pos;
   } else {
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_video_ro
       if (a.hg.heads[t] == hq) grp = gg;
   const int cnt = a.sel_count[(size_t)hq * a.rows_per_head + row_index];
   const int32_t* list = a.sel_idx + off;
-  const float* kc = (const float*)a.k_cube + (size_t)grp * g.N * D;
-  const float* vc = (const float*)a.v_cube + (size_t)grp * g.N * D;  // [Nc][D][S] per group
+  const float* kc = (const float*)a.k_cube + (size_t)grp * g.NS * D;
+  const float* vc = (const float*)a.v_cube + (size_t)grp * g.NS * D;  // [Nc][D][S] per group
   float M = -INFINITY, L = 0.f, o[PER] = {};
   // key sources: own cube (video), selected cubes, then causal text.
   // vat(key, e) reads value dim e of key `key` of the current source.

@@ -81,8 +81,8 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
   typedef __attribute__((address_space(3))) void lds_void;
 
   const uint32_t* rbits = a.extra_bits + (size_t)(hq * a.n_extra + m) * a.bits_words;
-  const char* kg = (const char*)a.k_cube + (size_t)grp * g.N * D * 2;
-  const char* vg = (const char*)a.v_cube + (size_t)grp * g.N * D * 2;  // [Nc][D][S]
+  const char* kg = (const char*)a.k_cube + (size_t)grp * g.NS * D * 2;
+  const char* vg = (const char*)a.v_cube + (size_t)grp * g.NS * D * 2;  // [Nc][D][S]
   const int c0 = chunk * a.extra_chunk_cubes;
   const int c1 = min(g.Nc, c0 + a.extra_chunk_cubes);
   for (int j = c0 + wv; j < c1; j += DW) {

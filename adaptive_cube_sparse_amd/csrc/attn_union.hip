@@ -160,7 +160,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // Q^T operand: row lr, d = 16*ds + 8*lh + [0..8)
   bf16x8u qb[D / 16];
   {
-    const uint16_t* src = video ? (const uint16_t*)a.q_cube + ((size_t)hq * g.N + pos) * D
+    const uint16_t* src = video ? (const uint16_t*)a.q_cube + ((size_t)hq * g.NS + pos) * D
                                 : (const uint16_t*)a.q_extra + ((size_t)pos * g.Hq + hq) * D;
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
@@ -480,11 +480,11 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   };
 
   const int nkb_cube = (g.S + UKB - 1) / UKB;
-  const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.N * D;
-  const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.N * D;  // [Nc][D][S] (ADAS_LAYOUT_VT)
+  const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.NS * D;
+  const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.NS * D;  // [Nc][D][S] (ADAS_LAYOUT_VT)
 
   // ---- own cube (video): every row ------------------------------------------------------
-  const char* vtg = (const char*)a.v_cube + (size_t)grp * g.N * D * 2;  // [Nc][D][S] per group
+  const char* vtg = (const char*)a.v_cube + (size_t)grp * g.NS * D * 2;  // [Nc][D][S] per group
   if (video) {
     if constexpr (FULL) {
       dpipeline(

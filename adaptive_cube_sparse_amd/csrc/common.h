@@ -22,6 +22,7 @@ struct KGeom {
   int S;     // tokens per cube
   int Nc;    // cubes
   int Hq, Hkv, D;
+  int NS;    // tokens per head in cube-layout buffers (capacity; N unless a cache is larger)
 };
 
 // Query heads grouped by the KV head they read.  Heads of group g are
@@ -328,6 +329,8 @@ hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, bool vt, con
                             void* dst, int32_t* perm, hipStream_t s);
 hipError_t launch_mean_keys(const KGeom& g, adas_dtype dt, const void* k, float* kbar,
                             hipStream_t s);
+hipError_t launch_cache_append(const KGeom& g, int f_lo, int f_hi, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, float* kbar, double* ksum, hipStream_t s);
 
 struct SelectArgs {
   KGeom g;

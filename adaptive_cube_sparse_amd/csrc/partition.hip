@@ -11,18 +11,20 @@ namespace adas {
 // One workgroup copies one cube of one head: S rows of `vpr` 16-byte vectors.
 // Rows are contiguous on both sides, so every 16-byte access is part of a
 // fully used row segment; the destination is written sequentially.
+// Frames [f_lo, f_hi) are copied (a whole tensor: 0, T); src holds those
+// frames only, in raster order, and blockIdx.x counts cubes from c_lo.
 __global__ __launch_bounds__(256) void k_partition(const uint4* __restrict__ src,
                                                    uint4* __restrict__ dst,
                                                    int32_t* __restrict__ perm, KGeom g, int nh,
-                                                   int vpr) {
-  const int c = blockIdx.x;
+                                                   int vpr, int f_lo, int f_hi, int c_lo) {
+  const int c = c_lo + blockIdx.x;
   const int h = blockIdx.y;
   // cube -> block coordinates (uniform per workgroup)
   const int bx = c % g.nW;
   const int by = (c / g.nW) % g.nH;
   const int bt = c / (g.nW * g.nH);
   const int hw = g.ch * g.cw;
-  const size_t dst_row0 = ((size_t)h * g.N + (size_t)c * g.S);
+  const size_t dst_row0 = ((size_t)h * g.NS + (size_t)c * g.S);
   const int total = g.S * vpr;
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
     const int r = e / vpr;
@@ -31,7 +33,9 @@ __global__ __launch_bounds__(256) void k_partition(const uint4* __restrict__ src
     const int rem = r - dt * hw;
     const int dy = rem / g.cw;
     const int dx = rem - dy * g.cw;
-    const int n = ((bt * g.ct + dt) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
+    const int f = bt * g.ct + dt;
+    if (f < f_lo || f >= f_hi) continue;
+    const int n = ((f - f_lo) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
     dst[(dst_row0 + r) * vpr + v] = src[((size_t)n * nh + h) * vpr + v];
     if (perm != nullptr && h == 0 && v == 0) perm[c * g.S + r] = n;
   }
@@ -43,17 +47,18 @@ __global__ __launch_bounds__(256) void k_partition(const uint4* __restrict__ src
 // vt_column(p), so consecutive threads write consecutive positions.
 template <typename T>
 __global__ __launch_bounds__(256) void k_partition_vt(const T* __restrict__ src, T* __restrict__ dst,
-                                                      int32_t* __restrict__ perm, KGeom g, int nh) {
+                                                      int32_t* __restrict__ perm, KGeom g, int nh,
+                                                      int f_lo, int f_hi, int c_lo) {
   constexpr int PAD = 4 / (int)sizeof(T);
   __shared__ T tile[64 * (128 + PAD)];
-  const int c = blockIdx.x;
+  const int c = c_lo + blockIdx.x;
   const int h = blockIdx.y;
   const int bx = c % g.nW;
   const int by = (c / g.nW) % g.nH;
   const int bt = c / (g.nW * g.nH);
   const int hw = g.ch * g.cw;
   const int D = g.D, TS = g.D + PAD;
-  T* out = dst + ((size_t)h * g.Nc + c) * (size_t)D * g.S;
+  T* out = dst + ((size_t)h * (g.NS / g.S) + c) * (size_t)D * g.S;
   for (int r0 = 0; r0 < g.S; r0 += 64) {
     const int nk = min(64, g.S - r0);
     __syncthreads();  // the previous chunk's reads of `tile` are done
@@ -64,35 +69,47 @@ __global__ __launch_bounds__(256) void k_partition_vt(const T* __restrict__ src,
       const int rem = r - dt * hw;
       const int dy = rem / g.cw;
       const int dx = rem - dy * g.cw;
-      const int n = ((bt * g.ct + dt) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
+      const int f = bt * g.ct + dt;
+      if (f < f_lo || f >= f_hi) continue;
+      const int n = ((f - f_lo) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
       tile[rr * TS + col] = src[((size_t)n * nh + h) * D + col];
       if (perm != nullptr && h == 0 && col == 0) perm[c * g.S + r] = n;
     }
     __syncthreads();
     for (int e = threadIdx.x; e < nk * D; e += blockDim.x) {
       const int d = e / nk, pl = e - d * nk;
-      const int rr = vt_column(r0 + pl, g.S) - r0;  // groups of 16 never straddle r0
-      out[(size_t)d * g.S + r0 + pl] = tile[rr * TS + d];
+      const int r = vt_column(r0 + pl, g.S);  // groups of 16 never straddle r0
+      const int f = bt * g.ct + r / hw;
+      if (f < f_lo || f >= f_hi) continue;
+      out[(size_t)d * g.S + r0 + pl] = tile[(r - r0) * TS + d];
     }
   }
 }
 
-hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, bool vt, const void* src,
-                            void* dst, int32_t* perm, hipStream_t s) {
-  dim3 grid(g.Nc, nh);
+hipError_t launch_partition_frames(const KGeom& g, int elem_bytes, int nh, bool vt, const void* src,
+                                   void* dst, int32_t* perm, int f_lo, int f_hi, hipStream_t s) {
+  const int per_block = g.nH * g.nW;
+  const int c_lo = f_lo / g.ct * per_block;
+  const int c_hi = ((f_hi - 1) / g.ct + 1) * per_block;
+  dim3 grid(c_hi - c_lo, nh);
   if (vt) {
     if (elem_bytes == 2)
       hipLaunchKernelGGL((k_partition_vt<uint16_t>), grid, dim3(256), 0, s, (const uint16_t*)src,
-                         (uint16_t*)dst, perm, g, nh);
+                         (uint16_t*)dst, perm, g, nh, f_lo, f_hi, c_lo);
     else
       hipLaunchKernelGGL((k_partition_vt<uint32_t>), grid, dim3(256), 0, s, (const uint32_t*)src,
-                         (uint32_t*)dst, perm, g, nh);
+                         (uint32_t*)dst, perm, g, nh, f_lo, f_hi, c_lo);
     return hipGetLastError();
   }
   const int vpr = g.D * elem_bytes / 16;
   hipLaunchKernelGGL(k_partition, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, g,
-                     nh, vpr);
+                     nh, vpr, f_lo, f_hi, c_lo);
   return hipGetLastError();
+}
+
+hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, bool vt, const void* src,
+                            void* dst, int32_t* perm, hipStream_t s) {
+  return launch_partition_frames(g, elem_bytes, nh, vt, src, dst, perm, 0, g.T, s);
 }
 
 // One wave per (kv head, cube).  Lanes are laid out LPR per row (16 bytes
@@ -112,7 +129,8 @@ __global__ __launch_bounds__(256) void k_mean_keys(const T* __restrict__ k, floa
   if (cube >= g.Hkv * g.Nc) return;
   const int col = (lane % LPR) * EPV;
   const int r0 = lane / LPR;
-  const T* base = k + (size_t)cube * g.S * D;  // (kv, j) cube rows are contiguous
+  const int kv = cube / g.Nc, j = cube - kv * g.Nc;
+  const T* base = k + ((size_t)kv * g.NS + (size_t)j * g.S) * D;  // the S rows of cube (kv, j)
   double acc[EPV];
 #pragma unroll
   for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
@@ -140,7 +158,7 @@ __global__ __launch_bounds__(256) void k_mean_keys(const T* __restrict__ k, floa
     float res[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) res[e] = (float)(acc[e] / (double)g.S);
-    float* dst = kbar + (size_t)cube * D + col;
+    float* dst = kbar + ((size_t)kv * (g.NS / g.S) + j) * D + col;
 #pragma unroll
     for (int e = 0; e < EPV; e += 4)
       *reinterpret_cast<float4*>(dst + e) = make_float4(res[e], res[e + 1], res[e + 2], res[e + 3]);
@@ -166,6 +184,66 @@ hipError_t launch_mean_keys(const KGeom& g, adas_dtype dt, const void* k, float*
       hipLaunchKernelGGL((k_mean_keys<float, 64>), grid, dim3(256), 0, s, (const float*)k, kbar,
                          g);
   }
+  return hipGetLastError();
+}
+
+// Streaming mean keys.  One wave per (kv head, cube of the temporal blocks
+// frames [f_lo, f_hi) touch); lane l owns columns l and l + 64 (D = 128) or
+// l (D = 64).  The rows of the new frames are summed in float64 from the
+// cache; a block that began before f_lo continues the running sums kept in
+// `ksum` (one slot per cube of a temporal block), and a block that ends by
+// f_hi gets its float32 mean key.  Sums of a cube's bf16 values are exact in
+// float64 (as for the one-pass mean keys), so the order of the partial sums
+// does not change the result.
+template <int D>
+__global__ __launch_bounds__(256) void k_stream_kbar(const uint16_t* __restrict__ k, float* __restrict__ kbar,
+                                                     double* __restrict__ ksum, KGeom g, int f_lo, int f_hi,
+                                                     int c_lo, int n_cubes) {
+  constexpr int CPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= g.Hkv * n_cubes) return;
+  const int kv = item / n_cubes;
+  const int c = c_lo + (item - kv * n_cubes);
+  const int per_block = g.nH * g.nW;
+  const int bt = c / per_block, slot = c - bt * per_block;
+  const int hw = g.ch * g.cw;
+  const int b0 = bt * g.ct, b1 = b0 + g.ct;  // frames of this cube
+  const int dt_lo = max(f_lo, b0) - b0, dt_hi = min(f_hi, b1) - b0;
+  double* run = ksum + ((size_t)kv * per_block + slot) * D;
+  double acc[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) acc[u] = (f_lo > b0) ? run[lane + 64 * u] : 0.0;
+  const uint16_t* base = k + ((size_t)kv * g.NS + (size_t)c * g.S) * D;
+  for (int r = dt_lo * hw; r < dt_hi * hw; ++r)
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) acc[u] += (double)bf16_bits_to_f32(base[(size_t)r * D + lane + 64 * u]);
+  if (f_hi >= b1) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u)
+      kbar[((size_t)kv * (g.NS / g.S) + c) * D + lane + 64 * u] = (float)(acc[u] / (double)g.S);
+  } else {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) run[lane + 64 * u] = acc[u];
+  }
+}
+
+hipError_t launch_cache_append(const KGeom& g, int f_lo, int f_hi, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, float* kbar, double* ksum, hipStream_t s) {
+  hipError_t e = launch_partition_frames(g, 2, g.Hkv, false, k_new, k_cache, nullptr, f_lo, f_hi, s);
+  if (e != hipSuccess) return e;
+  e = launch_partition_frames(g, 2, g.Hkv, true, v_new, v_cache, nullptr, f_lo, f_hi, s);
+  if (e != hipSuccess) return e;
+  const int per_block = g.nH * g.nW;
+  const int c_lo = f_lo / g.ct * per_block;
+  const int n_cubes = ((f_hi - 1) / g.ct + 1) * per_block - c_lo;
+  dim3 grid((g.Hkv * n_cubes + 3) / 4);
+  if (g.D == 128)
+    hipLaunchKernelGGL((k_stream_kbar<128>), grid, dim3(256), 0, s, (const uint16_t*)k_cache, kbar, ksum, g,
+                       f_lo, f_hi, c_lo, n_cubes);
+  else
+    hipLaunchKernelGGL((k_stream_kbar<64>), grid, dim3(256), 0, s, (const uint16_t*)k_cache, kbar, ksum, g,
+                       f_lo, f_hi, c_lo, n_cubes);
   return hipGetLastError();
 }
 

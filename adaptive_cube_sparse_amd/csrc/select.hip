@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (rr.hq >= 0 && n > 0) {
         const uint16_t* q = video
-            ? (const uint16_t*)a.q_cube + ((size_t)rr.hq * g.N + rr.pos) * D
+            ? (const uint16_t*)a.q_cube + ((size_t)rr.hq * g.NS + rr.pos) * D
             : (const uint16_t*)a.q_extra + ((size_t)rr.pos * g.Hq + rr.hq) * D;
         raw = *reinterpret_cast<const uint4*>(q + 32 * s + 8 * (lane / 16));
       }
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
     }
   }
   const float scale = 1.0f / sqrtf((float)D);
-  const float* kb = a.kbar + (size_t)grp * g.Nc * D;
+  const float* kb = a.kbar + (size_t)grp * (g.NS / g.S) * D;
   const int nblk = (n + 15) / 16;
   for (int blk = wave; blk < nblk; blk += kSelWaves) {
     const int j = blk * 16 + lane % 16;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void k_select_scores(SelectArgs a) {
   const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
   const int rows = gsz * a.n_extra;  // <= 64 on this path
   // 16-byte loads, all issued before any LDS store (the chunk is 64*D floats)
-  const float4* src = reinterpret_cast<const float4*>(a.kbar + ((size_t)grp * g.Nc + j0) * D);
+  const float4* src = reinterpret_cast<const float4*>(a.kbar + ((size_t)grp * (g.NS / g.S) + j0) * D);
   constexpr int NV = 64 * D / 4 / 256;
   float4 v[NV];
 #pragma unroll
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_vide
     const int pos = row_id - hq * g.N;
     const int c = pos / g.S;
     n = c;
-    q = (const float*)a.q_cube + ((size_t)hq * g.N + pos) * D;
+    q = (const float*)a.q_cube + ((size_t)hq * g.NS + pos) * D;
     off = video_list_offset(a.capv, hq, g.S, c, pos - c * g.S);
     row_index = pos;
   } else {
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_vide
   for (int gg = 0; gg < g.Hkv; ++gg)
     for (int t = a.hg.start[gg]; t < a.hg.start[gg + 1]; ++t)
       if (a.hg.heads[t] == hq) grp = gg;
-  const float* kb = a.kbar + (size_t)grp * g.Nc * D;
+  const float* kb = a.kbar + (size_t)grp * (g.NS / g.S) * D;
   const float scale = 1.0f / sqrtf((float)D);
   float E[NPL];
   float m = -INFINITY;

@@ -28,6 +28,10 @@
  *    thread-local message describing the last error is kept for
  *    adas_last_error().
  *  * Shapes: N = T*H*W tokens, S = ct*ch*cw tokens per cube, Nc = N / S cubes.
+ *    Cube-layout buffers (q_cube, k_cube, v_cube, kbar, x_cube) hold
+ *    NS = cT*H*W tokens (NS/S cubes) per head, cT = cache_T or T: head h
+ *    starts at token h*NS.  Only the first N tokens (Nc cubes) of a head are
+ *    read or written by a call.
  *    Cube c of raster token n = (f*H + y)*W + x is
  *    c = ((f/ct)*(H/ch) + y/ch)*(W/cw) + x/cw, its offset inside the cube is
  *    r = ((f%ct)*ch + y%ch)*cw + x%cw, and its cube-layout position is c*S + r.
@@ -75,6 +79,10 @@ typedef struct {
   int32_t n_kv_heads;       /* Hkv                                            */
   int32_t head_dim;         /* d_k (64 or 128)                                */
   const int32_t* head_map;  /* HOST array [Hq] -> kv head, or NULL            */
+  int32_t cache_T;          /* frames each head of a cube-layout buffer holds:
+                               0 = T; else a multiple of ct, >= T (a video KV
+                               cache allocated for cache_T frames of which the
+                               first T are filled, see adas_cache_append)     */
 } adas_geom;
 
 /* Which call a workspace is sized for. */
@@ -205,6 +213,38 @@ adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const 
                                  const void* v_text, const int32_t* sel_count,
                                  const int32_t* sel_idx, void* out_raster, void* out_extra,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * adas_cache_append -- grow a video KV cache while decoding: frames arrive in
+ * order and are written straight into the cube layout, and the mean key of
+ * every cube is formed as soon as its last frame arrives (streaming extension
+ * of key designs 1 and 2; selection needs a cube's mean key, so a cube is
+ * selectable once its temporal block is complete).
+ *   geom      the whole cache: T = frames the cache can hold (or cache_T);
+ *             bf16 only
+ *   t0        frames already in the cache (0 for the first call)
+ *   n_frames  frames in this call; t0 + n_frames <= capacity
+ *   k_new, v_new [n_frames*H*W][Hkv][d]  the new frames' keys and values,
+ *             raster order within the new frames
+ *   k_cache   [Hkv][NS][d] (ADAS_LAYOUT_TOKENS), v_cache [Hkv][NS/S][d][S]
+ *             (ADAS_LAYOUT_VT), kbar [Hkv][NS/S][d] float32
+ *   ksum      float64 running sums of the unfinished temporal block,
+ *             adas_cache_sum_bytes() bytes, caller-owned, kept between calls
+ *             (no initialisation needed: a block that starts in a call starts
+ *             from zero)
+ * After the call the first t0 + n_frames frames of the cache are laid out as
+ * adas_cube_partition lays out the whole prefix, and kbar holds the mean
+ * keys of every cube of the completed temporal blocks, bit-identical to
+ * adas_cube_mean_keys.  Decode then uses a geometry with T = the completed
+ * frames and cache_T = the capacity.
+ * Errors: NULL, SHAPE (frame range, grid), DTYPE (not bf16), HIP.
+ */
+adas_status adas_cache_append(const adas_geom* geom, adas_dtype dtype, int32_t t0, int32_t n_frames,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              float* kbar, double* ksum, void* stream);
+
+/* Bytes of the running-sum state adas_cache_append keeps (host only). */
+size_t adas_cache_sum_bytes(const adas_geom* geom);
 
 /* Bytes of workspace `kind` needs (host only, no device work).  has_video is
  * 1 when q_cube will be non-NULL.  Returns 0 for invalid geometry. */

@@ -197,3 +197,26 @@ def test_ffn_workspace_closed_form_and_host_validation():
     assert fwd(need - 1) == L.ADAS_ERR_WORKSPACE
     assert fwd(need, inter=320) == L.ADAS_ERR_SHAPE
     assert fwd(need, n_text=3) == L.ADAS_ERR_NULL
+
+
+def test_cache_geometry_and_append_validation():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails on the host
+    g = _geom(T=8, cache_T=12)
+    # cache_T must be 0 or a multiple of ct that is >= T
+    for bad in (4, 10):
+        gb = _geom(T=8, cache_T=bad)
+        assert lib.adas_sel_capacity(ctypes.byref(gb), 0, 1) == -1
+    assert lib.adas_sel_capacity(ctypes.byref(g), 0, 1) > 0
+    # running sums: Hkv * nH * nW * d doubles
+    assert lib.adas_cache_sum_bytes(ctypes.byref(g)) == 2 * 4 * 4 * 128 * 8
+    def app(t0, n, dtype=None):
+        return lib.adas_cache_append(ctypes.byref(g), L.ADAS_BF16 if dtype is None else dtype, t0, n,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert app(0, 0) == L.ADAS_ERR_SHAPE
+    assert app(10, 3) == L.ADAS_ERR_SHAPE          # past the capacity of 12 frames
+    assert app(-1, 2) == L.ADAS_ERR_SHAPE
+    assert app(0, 4, L.ADAS_F32) == L.ADAS_ERR_DTYPE
+    assert lib.adas_cache_append(ctypes.byref(g), L.ADAS_BF16, 0, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == L.ADAS_ERR_NULL
