@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     ADAS_BF16, ADAS_F32, ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT, ADAS_WS_ATTN, ADAS_WS_SELECT,
     AdasError, FfnGeometry, Geometry, LIB_PATH,
     adas_ffn_fwd, adas_ffn_select, adas_ffn_workspace_bytes, adas_cache_append, adas_cache_sum_bytes,
+    adas_sparse_attn_fwd_lse, adas_sparse_attn_bwd, ADAS_WS_BWD,
     adas_cube_mean_keys, adas_cube_partition, adas_select_topk, adas_select_topp, adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
 )
@@ -38,6 +39,7 @@ __all__ = [
     "adas_version", "load", "LIB_PATH",
     "FfnGeometry", "AdasFFN", "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "StreamingCache",
+    "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd", "AdasAttentionGrad",
 ]
 
 
@@ -221,3 +223,47 @@ class StreamingCache:
         adas_sparse_attn_fwd(g, None, self.k_cache, self.v_cache, q_extra, None, None, cnt, idx, None, out,
                              ws_a, stream)
         return out, cnt, idx
+
+
+class AdasAttentionGrad:
+    """Forward with log-sum-exp and backward of the sparse attention for one
+    layer (video rows, and extra rows that attend their selected cubes only):
+    the fine-tuning step the AdaSpark pages adapt the backbone with.  The
+    selection is computed in the forward and held fixed in the backward."""
+
+    def __init__(self, geom: Geometry, p: float, has_video: bool = True, n_extra: int = 0, device="cuda",
+                 topk: Optional[int] = None):
+        self.fwd = AdasAttention(geom, torch.bfloat16, p, has_video=has_video, n_extra=n_extra,
+                                 device=device, topk=topk)
+        g = geom
+        dev = torch.device(device)
+        e = dict(device=dev, dtype=torch.bfloat16)
+        self.v_tok = torch.empty((g.n_kv_heads, g.NS, g.head_dim), **e)
+        self.k_vt = torch.empty((g.n_kv_heads, g.NS // g.S, g.head_dim, g.S), **e)
+        self.lse = torch.empty(tuple(self.fwd.sel_count.shape), device=dev, dtype=torch.float32)
+        f = dict(device=dev, dtype=torch.float32)
+        self.dq = torch.empty((g.N, g.n_q_heads, g.head_dim), **f) if has_video else None
+        self.dq_extra = torch.empty((n_extra, g.n_q_heads, g.head_dim), **f) if n_extra else None
+        self.dk = torch.empty((g.N, g.n_kv_heads, g.head_dim), **f)
+        self.dv = torch.empty((g.N, g.n_kv_heads, g.head_dim), **f)
+        ws = adas_workspace_bytes(g, torch.bfloat16, ADAS_WS_BWD, has_video, n_extra)
+        self.ws_bwd = torch.empty((ws,), device=dev, dtype=torch.uint8)
+
+    def forward(self, q_raster, k_raster, v_raster, q_extra=None, stream=None):
+        L = self.fwd
+        L.build_kv(k_raster, v_raster, stream)
+        adas_cube_partition(L.geom, v_raster, self.v_tok, None, stream)
+        adas_cube_partition(L.geom, k_raster, self.k_vt, None, stream, layout=ADAS_LAYOUT_VT)
+        if L.has_video:
+            L.partition_queries(q_raster, stream)
+        L.select(q_extra, stream=stream)
+        adas_sparse_attn_fwd_lse(L.geom, L.q_cube, L.k_cube, L.v_cube, q_extra, None, None, L.sel_count,
+                                 L.sel_idx, L.out_raster, L.out_extra, self.lse, L.ws, stream)
+        return L.out_raster, L.out_extra
+
+    def backward(self, dout_raster, dout_extra=None, q_extra=None, stream=None):
+        L = self.fwd
+        adas_sparse_attn_bwd(L.geom, L.q_cube, L.k_cube, self.v_tok, self.k_vt, q_extra, L.sel_count, L.sel_idx,
+                             L.out_raster, L.out_extra, self.lse, dout_raster, dout_extra, self.dq, self.dq_extra,
+                             self.dk, self.dv, self.ws_bwd, stream)
+        return self.dq, self.dq_extra, self.dk, self.dv

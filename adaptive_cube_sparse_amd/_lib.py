@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libadas.so")
 ADAS_OK, ADAS_ERR_NULL, ADAS_ERR_SHAPE, ADAS_ERR_VALUE, ADAS_ERR_DTYPE, \
     ADAS_ERR_WORKSPACE, ADAS_ERR_CAPACITY, ADAS_ERR_HIP = range(8)
 ADAS_BF16, ADAS_F32 = 0, 1
-ADAS_WS_SELECT, ADAS_WS_ATTN = 0, 1
+ADAS_WS_SELECT, ADAS_WS_ATTN, ADAS_WS_BWD = 0, 1, 2
 ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT = 0, 1
 ADAS_MAX_HEADS = 128
 ADAS_MAX_CUBES = 4096
@@ -31,7 +31,7 @@ EXPORTS = (
     "adas_sparse_attn_fwd", "adas_workspace_bytes", "adas_sel_capacity",
     "adas_status_string", "adas_last_error", "adas_version",
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
-    "adas_cache_append", "adas_cache_sum_bytes",
+    "adas_cache_append", "adas_cache_sum_bytes", "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd",
 )
 
 
@@ -84,6 +84,10 @@ def load() -> ctypes.CDLL:
         "adas_ffn_workspace_bytes": (sz, [fgp, i32]),
         "adas_cache_append": (i32, [gp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
         "adas_cache_sum_bytes": (sz, [gp]),
+        "adas_sparse_attn_fwd_lse": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, sz, vp]),
+        "adas_sparse_attn_bwd": (i32, [gp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -320,6 +324,64 @@ def adas_cache_sum_bytes(geom: Geometry) -> int:
     lib = load()
     g, keep = geom._c()
     return int(lib.adas_cache_sum_bytes(ctypes.byref(g)))
+
+
+def adas_sparse_attn_fwd_lse(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text, v_text,
+                             sel_count, sel_idx, out_raster, out_extra, lse,
+                             ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """adas_sparse_attn_fwd that also writes each row's log-sum-exp to
+    lse [Hq][rows] (float32)."""
+    lib = load()
+    ref = q_cube if q_cube is not None else q_extra
+    n_extra = 0 if q_extra is None else q_extra.shape[0]
+    n_text_kv = 0 if k_text is None else k_text.shape[0]
+    Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
+    _shape(q_cube, (Hq, geom.NS, d), "q_cube")
+    _shape(k_cube, (Hkv, geom.NS, d), "k_cube")
+    _shape(v_cube, (Hkv, geom.NS // geom.S, d, geom.S), "v_cube")
+    _shape(lse, tuple(sel_count.shape), "lse")
+    dt = ref.dtype
+    g, keep = geom._c()
+    st = lib.adas_sparse_attn_fwd_lse(
+        ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, dt, "q_cube"), _ptr(k_cube, dt, "k_cube"),
+        _ptr(v_cube, dt, "v_cube"), n_extra, n_text_kv, _ptr(q_extra, dt, "q_extra"),
+        _ptr(k_text, dt, "k_text"), _ptr(v_text, dt, "v_text"),
+        _ptr(sel_count, torch.int32, "sel_count"), _ptr(sel_idx, torch.int32, "sel_idx"),
+        _ptr(out_raster, dt, "out_raster"), _ptr(out_extra, dt, "out_extra"), _ptr(lse, torch.float32, "lse"),
+        _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "adas_sparse_attn_fwd_lse")
+
+
+def adas_sparse_attn_bwd(geom: Geometry, q_cube, k_cube, v_tok, k_vt, q_extra, sel_count, sel_idx,
+                         out_raster, out_extra, lse, dout_raster, dout_extra, dq_raster, dq_extra,
+                         dk_raster, dv_raster, ws: torch.Tensor, stream=None) -> None:
+    """Gradients of the sparse attention with the selection held fixed; see
+    adas.h (bf16 inputs, float32 gradients in raster order)."""
+    lib = load()
+    n_extra = 0 if q_extra is None else q_extra.shape[0]
+    Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
+    bf, f32 = torch.bfloat16, torch.float32
+    _shape(q_cube, (Hq, geom.NS, d), "q_cube")
+    _shape(k_cube, (Hkv, geom.NS, d), "k_cube")
+    _shape(v_tok, (Hkv, geom.NS, d), "v_tok")
+    _shape(k_vt, (Hkv, geom.NS // geom.S, d, geom.S), "k_vt")
+    _shape(dk_raster, (geom.N, Hkv, d), "dk_raster")
+    _shape(dv_raster, (geom.N, Hkv, d), "dv_raster")
+    if q_cube is not None:
+        _shape(dq_raster, (geom.N, Hq, d), "dq_raster")
+        _shape(dout_raster, (geom.N, Hq, d), "dout_raster")
+    if n_extra:
+        _shape(dq_extra, (n_extra, Hq, d), "dq_extra")
+        _shape(dout_extra, (n_extra, Hq, d), "dout_extra")
+    g, keep = geom._c()
+    st = lib.adas_sparse_attn_bwd(
+        ctypes.byref(g), ADAS_BF16, _ptr(q_cube, bf, "q_cube"), _ptr(k_cube, bf, "k_cube"), _ptr(v_tok, bf, "v_tok"),
+        _ptr(k_vt, bf, "k_vt"), n_extra, _ptr(q_extra, bf, "q_extra"), _ptr(sel_count, torch.int32, "sel_count"),
+        _ptr(sel_idx, torch.int32, "sel_idx"), _ptr(out_raster, bf, "out_raster"), _ptr(out_extra, bf, "out_extra"),
+        _ptr(lse, f32, "lse"), _ptr(dout_raster, bf, "dout_raster"), _ptr(dout_extra, bf, "dout_extra"),
+        _ptr(dq_raster, f32, "dq_raster"), _ptr(dq_extra, f32, "dq_extra"), _ptr(dk_raster, f32, "dk_raster"),
+        _ptr(dv_raster, f32, "dv_raster"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "adas_sparse_attn_bwd")
 
 
 def adas_workspace_bytes(geom: Geometry, dtype: torch.dtype, kind: int, has_video: bool,

@@ -208,6 +208,7 @@ adas_status adas_select_topk(const adas_geom* geom, adas_dtype dtype, const void
 
 static adas_status build_attn(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
                               int32_t n_extra, int32_t n_text_kv, adas::AttnArgs& a) {
+  a = adas::AttnArgs{};
   adas_status st = derive(geom, a.g, a.hg);
   if (st != ADAS_OK) return st;
   if ((st = check_dtype(dtype)) != ADAS_OK) return st;
@@ -226,12 +227,12 @@ static adas_status build_attn(const adas_geom* geom, adas_dtype dtype, const voi
   return ADAS_OK;
 }
 
-adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
-                                 const void* k_cube, const void* v_cube, int32_t n_extra,
-                                 int32_t n_text_kv, const void* q_extra, const void* k_text,
-                                 const void* v_text, const int32_t* sel_count,
-                                 const int32_t* sel_idx, void* out_raster, void* out_extra,
-                                 void* ws, size_t ws_bytes, void* stream) {
+static adas_status attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                            const void* k_cube, const void* v_cube, int32_t n_extra,
+                            int32_t n_text_kv, const void* q_extra, const void* k_text,
+                            const void* v_text, const int32_t* sel_count,
+                            const int32_t* sel_idx, void* out_raster, void* out_extra,
+                            float* lse, void* ws, size_t ws_bytes, void* stream) {
   adas::AttnArgs a;
   adas_status st = build_attn(geom, dtype, q_cube, n_extra, n_text_kv, a);
   if (st != ADAS_OK) return st;
@@ -255,9 +256,90 @@ adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const 
   a.sel_idx = sel_idx;
   a.out_raster = out_raster;
   a.out_extra = out_extra;
+  a.lse = lse;
   adas::bind_attention_workspace(a, dtype, ws);
   return hip_status(adas::launch_attention(a, dtype, (hipStream_t)stream),
                     "adas_sparse_attn_fwd launch");
+}
+
+adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                 const void* k_cube, const void* v_cube, int32_t n_extra,
+                                 int32_t n_text_kv, const void* q_extra, const void* k_text,
+                                 const void* v_text, const int32_t* sel_count,
+                                 const int32_t* sel_idx, void* out_raster, void* out_extra,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd(geom, dtype, q_cube, k_cube, v_cube, n_extra, n_text_kv, q_extra, k_text, v_text,
+                  sel_count, sel_idx, out_raster, out_extra, nullptr, ws, ws_bytes, stream);
+}
+
+adas_status adas_sparse_attn_fwd_lse(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                     const void* k_cube, const void* v_cube, int32_t n_extra,
+                                     int32_t n_text_kv, const void* q_extra, const void* k_text,
+                                     const void* v_text, const int32_t* sel_count,
+                                     const int32_t* sel_idx, void* out_raster, void* out_extra,
+                                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (lse == nullptr) return fail(ADAS_ERR_NULL, "lse is NULL");
+  return attn_fwd(geom, dtype, q_cube, k_cube, v_cube, n_extra, n_text_kv, q_extra, k_text, v_text,
+                  sel_count, sel_idx, out_raster, out_extra, lse, ws, ws_bytes, stream);
+}
+
+static adas_status build_bwd(const adas_geom* geom, adas_dtype dtype, bool has_video, int32_t n_extra,
+                             adas::BwdArgs& b) {
+  b = adas::BwdArgs{};
+  adas_status st = derive(geom, b.g, b.hg);
+  if (st != ADAS_OK) return st;
+  if (dtype != ADAS_BF16) return fail(ADAS_ERR_DTYPE, "the backward supports bf16 only");
+  if (b.g.S != 64)
+    return fail(ADAS_ERR_SHAPE, "the backward is enabled for cubes of 64 tokens only (S = %d)", b.g.S);
+  if (b.g.Nc > ADAS_MAX_CUBES) return fail(ADAS_ERR_SHAPE, "%d cubes exceed the limit %d", b.g.Nc, ADAS_MAX_CUBES);
+  if (n_extra < 0) return fail(ADAS_ERR_SHAPE, "n_extra must be >= 0");
+  if (!has_video && n_extra == 0) return fail(ADAS_ERR_SHAPE, "no query rows");
+  b.has_video = has_video;
+  b.n_extra = n_extra;
+  b.capv = capv_of(b.g, has_video);
+  b.rows_per_head = (has_video ? b.g.N : 0) + n_extra;
+  adas::plan_backward(b);
+  return ADAS_OK;
+}
+
+adas_status adas_sparse_attn_bwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                 const void* k_cube, const void* v_tok, const void* k_vt, int32_t n_extra,
+                                 const void* q_extra, const int32_t* sel_count, const int32_t* sel_idx,
+                                 const void* out_raster, const void* out_extra, const float* lse,
+                                 const void* dout_raster, const void* dout_extra, float* dq_raster,
+                                 float* dq_extra, float* dk_raster, float* dv_raster, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  adas::BwdArgs b;
+  adas_status st = build_bwd(geom, dtype, q_cube != nullptr, n_extra, b);
+  if (st != ADAS_OK) return st;
+  if (k_cube == nullptr || v_tok == nullptr || k_vt == nullptr || sel_count == nullptr || sel_idx == nullptr ||
+      lse == nullptr || dk_raster == nullptr || dv_raster == nullptr)
+    return fail(ADAS_ERR_NULL, "k_cube/v_tok/k_vt/sel_count/sel_idx/lse/dk_raster/dv_raster is NULL");
+  if (q_cube != nullptr && (out_raster == nullptr || dout_raster == nullptr || dq_raster == nullptr))
+    return fail(ADAS_ERR_NULL, "out_raster/dout_raster/dq_raster is NULL");
+  if (n_extra > 0 && (q_extra == nullptr || out_extra == nullptr || dout_extra == nullptr || dq_extra == nullptr))
+    return fail(ADAS_ERR_NULL, "q_extra/out_extra/dout_extra/dq_extra is NULL");
+  const size_t need = adas::backward_workspace_bytes(b);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  b.q_cube = (const uint16_t*)q_cube;
+  b.q_extra = (const uint16_t*)q_extra;
+  b.k_cube = (const uint16_t*)k_cube;
+  b.v_tok = (const uint16_t*)v_tok;
+  b.k_vt = (const uint16_t*)k_vt;
+  b.out_raster = (const uint16_t*)out_raster;
+  b.out_extra = (const uint16_t*)out_extra;
+  b.dout_raster = (const uint16_t*)dout_raster;
+  b.dout_extra = (const uint16_t*)dout_extra;
+  b.lse = lse;
+  b.sel_count = sel_count;
+  b.sel_idx = sel_idx;
+  b.dq_raster = dq_raster;
+  b.dq_extra = dq_extra;
+  b.dk_raster = dk_raster;
+  b.dv_raster = dv_raster;
+  adas::bind_backward_workspace(b, ws);
+  return hip_status(adas::launch_backward(b, (hipStream_t)stream), "adas_sparse_attn_bwd launch");
 }
 
 adas_status adas_cache_append(const adas_geom* geom, adas_dtype dtype, int32_t t0, int32_t n_frames,
@@ -299,6 +381,11 @@ size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kin
     if (derive(geom, g, hg) != ADAS_OK || check_dtype(dtype) != ADAS_OK) return 0;
     if (n_extra < 0) return 0;
     return adas::select_workspace_bytes(g, dtype, n_extra, hg.gmax);
+  }
+  if (kind == ADAS_WS_BWD) {
+    adas::BwdArgs b;
+    if (build_bwd(geom, dtype, has_video != 0, n_extra, b) != ADAS_OK) return 0;
+    return adas::backward_workspace_bytes(b);
   }
   adas::AttnArgs a;
   const int dummy = 1;

@@ -67,6 +67,8 @@ __global__ __launch_bounds__(256) void k_merge_bf16(AttnArgs a, int n_tiles) {
   __syncthreads();
   if (wave != 0) return;
   const float Lt = red_o[0][D] + red_o[1][D] + red_o[2][D] + red_o[3][D];
+  if (a.lse != nullptr && lane == 0)
+    a.lse[(size_t)hq * a.rows_per_head + (a.has_video ? a.g.N : 0) + m] = (M + __log2f(Lt)) * 0.69314718055994531f;
   uint16_t* dst = (uint16_t*)a.out_extra + ((size_t)m * a.g.Hq + hq) * D + lane * PER;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -187,6 +189,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int total_video_ro
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) dst[lane * PER + i] = o[i] / L;
+  if (a.lse != nullptr && lane == 0)
+    a.lse[(size_t)hq * a.rows_per_head + row_index] = (M + __log2f(L)) * 0.69314718055994531f;
 }
 
 // ---------------------------------------------------------------------------

@@ -668,6 +668,9 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     return;
   }
   const float inv = 1.0f / l_run;
+  if (a.lse != nullptr && lh == 0)
+    a.lse[(size_t)hq * a.rows_per_head + (video ? pos : (a.has_video ? g.N : 0) + pos)] =
+        (m_run + __log2f(l_run)) * 0.69314718055994531f;
   uint16_t* dst;
   if (video) {
     const int n = raster_of(g, c, pos - c * g.S);

@@ -86,7 +86,7 @@ typedef struct {
 } adas_geom;
 
 /* Which call a workspace is sized for. */
-typedef enum { ADAS_WS_SELECT = 0, ADAS_WS_ATTN = 1 } adas_ws_kind;
+typedef enum { ADAS_WS_SELECT = 0, ADAS_WS_ATTN = 1, ADAS_WS_BWD = 2 } adas_ws_kind;
 
 /* Storage of a cube-layout tensor (see adas_cube_partition). */
 typedef enum { ADAS_LAYOUT_TOKENS = 0, ADAS_LAYOUT_VT = 1 } adas_layout;
@@ -213,6 +213,48 @@ adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const 
                                  const void* v_text, const int32_t* sel_count,
                                  const int32_t* sel_idx, void* out_raster, void* out_extra,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * adas_sparse_attn_fwd_lse -- adas_sparse_attn_fwd that also stores each
+ * row's log-sum-exp, the statistic adas_sparse_attn_bwd needs.
+ *   lse  [Hq][R] float32 (R and row order as sel_count): natural log of
+ *        sum_j exp(q.k_j / sqrt(d)) over the row's attended keys
+ * Errors: as adas_sparse_attn_fwd; NULL for lse.
+ */
+adas_status adas_sparse_attn_fwd_lse(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                     const void* k_cube, const void* v_cube, int32_t n_extra,
+                                     int32_t n_text_kv, const void* q_extra, const void* k_text,
+                                     const void* v_text, const int32_t* sel_count,
+                                     const int32_t* sel_idx, void* out_raster, void* out_extra,
+                                     float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * adas_sparse_attn_bwd -- gradients of the sparse attention for fine-tuning
+ * on the sparse pattern (papernotes.org, training strategy; key design 2
+ * attention).  The selection is a discrete choice and is held fixed: no
+ * gradient reaches it or the mean keys.  Rows: video rows (selected cubes +
+ * own cube) and extra rows (selected cubes only; the causal text keys of a
+ * text prefill are not covered).  bf16 only, cubes of S = 64 tokens.
+ *   q_cube, k_cube [h][NS][d]      ADAS_LAYOUT_TOKENS (q_cube NULL: no video rows)
+ *   v_tok    [Hkv][NS][d]          V in ADAS_LAYOUT_TOKENS
+ *   k_vt     [Hkv][NS/S][d][S]     K in ADAS_LAYOUT_VT
+ *   n_extra, q_extra, sel_count, sel_idx   as adas_sparse_attn_fwd
+ *   out_raster, out_extra, lse     the forward's outputs (adas_sparse_attn_fwd_lse)
+ *   dout_raster [N][Hq][d], dout_extra [n_extra][Hq][d]   their gradients (bf16)
+ *   dq_raster [N][Hq][d], dq_extra [n_extra][Hq][d],
+ *   dk_raster, dv_raster [N][Hkv][d]   float32 outputs, raster token order;
+ *            every element is written (keys no row attends get 0)
+ *   ws, ws_bytes  adas_workspace_bytes(ADAS_WS_BWD, ...): per-row D, the
+ *            selections as bitmaps, and per cube the list of rows attending it
+ * Errors: NULL, SHAPE (S != 64, Nc), DTYPE (not bf16), WORKSPACE, HIP.
+ */
+adas_status adas_sparse_attn_bwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                 const void* k_cube, const void* v_tok, const void* k_vt, int32_t n_extra,
+                                 const void* q_extra, const int32_t* sel_count, const int32_t* sel_idx,
+                                 const void* out_raster, const void* out_extra, const float* lse,
+                                 const void* dout_raster, const void* dout_extra, float* dq_raster,
+                                 float* dq_extra, float* dk_raster, float* dv_raster, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /*
  * adas_cache_append -- grow a video KV cache while decoding: frames arrive in

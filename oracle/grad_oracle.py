@@ -29,7 +29,7 @@ import numpy as np
 
 from .adas_oracle import Geometry, _kv_head, cube_coords, to_f64
 
-__all__ = ["attend_grad", "attention_grads"]
+__all__ = ["attend_grad", "attention_grads", "row_weights"]
 
 
 def attend_grad(q: np.ndarray, keys: np.ndarray, values: np.ndarray, do: np.ndarray):
@@ -48,6 +48,17 @@ def attend_grad(q: np.ndarray, keys: np.ndarray, values: np.ndarray, do: np.ndar
     dq = c * (ds @ keys)
     dk = c * np.outer(ds, q)
     return o, m + math.log(z), dq, dk, dv
+
+
+def row_weights(q: np.ndarray, keys: np.ndarray, values: np.ndarray, do: np.ndarray):
+    """The softmax weights p and score gradients ds of one row (the same
+    quantities attend_grad forms), for bounding rounding effects in tests."""
+    c = 1.0 / math.sqrt(q.shape[-1])
+    s = c * (keys @ q)
+    e = np.exp(s - s.max())
+    p = e / e.sum()
+    dp = values @ do
+    return p, p * (dp - float(p @ dp))
 
 
 def attention_grads(q_cube, k_cube, v_cube, g: Geometry, sel_video: dict, dout_raster,
