@@ -10,6 +10,7 @@
 
 #include "adas.h"
 #include "adas_ffn.h"
+#include "attn_bwd.h"
 #include "common.h"
 #include "ffn.h"
 

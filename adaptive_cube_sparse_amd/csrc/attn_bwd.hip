@@ -21,7 +21,7 @@
 //                partial sums are added through LDS at the end.
 #include <type_traits>
 
-#include "common.h"
+#include "attn_bwd.h"
 
 namespace adas {
 
@@ -424,11 +424,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int R = a.rows_per_head;
   const int Nv = a.has_video ? g.N : 0;
   const int nkb = g.S / BKB;
-  // heaviest first: ascending cube (earlier cubes are attended by more rows)
-  const int per_c = g.Hkv * nkb;
-  const int j = blockIdx.x / per_c;
-  const int rem = blockIdx.x - j * per_c;
-  const int grp = rem / nkb, kbi = rem - grp * nkb;
+  // KV head by KV head, so that the rows gathered at any one time are those
+  // of one head group (they then stay in the memory-side cache); within a
+  // head heaviest first: ascending cube (earlier cubes are attended by more
+  // rows)
+  const int per_g = g.Nc * nkb;
+  const int grp = blockIdx.x / per_g;
+  const int rem = blockIdx.x - grp * per_g;
+  const int j = rem / nkb, kbi = rem - j * nkb;
   const int key0 = j * g.S + kbi * BKB;  // first key (cube-layout position)
   // K and V rows of the block into LDS
   for (int e = tid; e < BKB * D / 8; e += 256) {
@@ -452,51 +455,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   uint16_t* Tdo = tdo[wave];
   const int pcol = vt_column(lr, 32);  // transposed column of this lane's row
   const int ntiles = (cnt + 31) / 32;
-  for (int t = wave; t < ntiles; t += 4) {
-    // this lane's row of the tile
-    const int idx = t * 32 + lr;
-    const bool ok = idx < cnt;
-    int hq = 0, rr = 0;
-    const uint16_t *qs = nullptr, *ds_ = nullptr;
-    if (ok) {
-      const int id = list[idx];
-      hq = id / R;
-      rr = id - hq * R;
-      if (rr < Nv) {
-        const int c = rr / g.S;
-        const size_t n = (size_t)raster_of(g, c, rr - c * g.S);
-        qs = a.q_cube + ((size_t)hq * g.NS + rr) * D;
-        ds_ = a.dout_raster + (n * g.Hq + hq) * D;
-      } else {
-        const int m = rr - Nv;
-        qs = a.q_extra + ((size_t)m * g.Hq + hq) * D;
-        ds_ = a.dout_extra + ((size_t)m * g.Hq + hq) * D;
-      }
+  // Tile t's rows are list entries 32t..32t+31.  Lanes past the list take the
+  // last entry (a valid row with finite values) and are given an infinite
+  // log2 LSE (P = 0) and D = 0, so they add nothing; every load is therefore
+  // unconditional and none waits before its value is used.  List entries run
+  // two tiles ahead of the rows and rows one tile ahead of the compute.
+  auto entry = [&](int t) __attribute__((always_inline)) {
+    return list[min(t * 32 + lr, cnt - 1)];
+  };
+  uint4 qraw[D / 16], draw[D / 16];
+  float lraw = 0.f, draw_d = 0.f;
+  auto fetch = [&](int id) __attribute__((always_inline)) {
+    const int hq = id / R, rr = id - hq * R;
+    const uint16_t *qs, *ds_;
+    if (rr < Nv) {
+      const int c = rr / g.S;
+      const size_t n = (size_t)raster_of(g, c, rr - c * g.S);
+      qs = a.q_cube + ((size_t)hq * g.NS + rr) * D;
+      ds_ = a.dout_raster + (n * g.Hq + hq) * D;
+    } else {
+      const int m = rr - Nv;
+      qs = a.q_extra + ((size_t)m * g.Hq + hq) * D;
+      ds_ = a.dout_extra + ((size_t)m * g.Hq + hq) * D;
     }
-    bbf16x8 qa[D / 16], da[D / 16];
-    uint4 qraw[D / 16], draw[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      qraw[s] = make_uint4(0, 0, 0, 0);
-      draw[s] = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        qraw[s] = *reinterpret_cast<const uint4*>(qs + 16 * s + 8 * lh);
-        draw[s] = *reinterpret_cast<const uint4*>(ds_ + 16 * s + 8 * lh);
-      }
-      qa[s] = __builtin_bit_cast(bbf16x8, qraw[s]);
-      da[s] = __builtin_bit_cast(bbf16x8, draw[s]);
+      qraw[s] = *reinterpret_cast<const uint4*>(qs + 16 * s + 8 * lh);
+      draw[s] = *reinterpret_cast<const uint4*>(ds_ + 16 * s + 8 * lh);
+    }
+    lraw = a.lse[(size_t)hq * R + rr];
+    draw_d = a.delta[(size_t)hq * R + rr];
+  };
+  int idn = 0;
+  if (ntiles > wave) {
+    fetch(entry(wave));
+    if (wave + 4 < ntiles) idn = entry(wave + 4);
+  }
+  for (int t = wave; t < ntiles; t += 4) {
+    // the current tile's operands; the next tile's loads fly during its MFMAs
+    bbf16x8 qa[D / 16], da[D / 16];
+    uint4 qcur[D / 16], dcur[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qcur[s] = qraw[s];
+      dcur[s] = draw[s];
+      qa[s] = __builtin_bit_cast(bbf16x8, qcur[s]);
+      da[s] = __builtin_bit_cast(bbf16x8, dcur[s]);
     }
     if (lh == 0) {
-      // rows past the list get an infinite LSE (P = 0) and D = 0
-      rinfo[wave][0][lr] = ok ? a.lse[(size_t)hq * R + rr] * kBLog2e : INFINITY;
-      rinfo[wave][1][lr] = ok ? a.delta[(size_t)hq * R + rr] : 0.f;
+      const bool ok = t * 32 + lr < cnt;
+      rinfo[wave][0][lr] = ok ? lraw * kBLog2e : INFINITY;
+      rinfo[wave][1][lr] = ok ? draw_d : 0.f;
+    }
+    if (t + 4 < ntiles) {
+      fetch(idn);
+      if (t + 8 < ntiles) idn = entry(t + 8);
     }
     // transposed copies: T[d][pcol] = row value at d (16-bit halves taken
     // from the raw words)
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const uint32_t qw[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
-      const uint32_t dw[4] = {draw[s].x, draw[s].y, draw[s].z, draw[s].w};
+      const uint32_t qw[4] = {qcur[s].x, qcur[s].y, qcur[s].z, qcur[s].w};
+      const uint32_t dw[4] = {dcur[s].x, dcur[s].y, dcur[s].z, dcur[s].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = 16 * s + 8 * lh + i;

@@ -23,6 +23,13 @@ is instead one AdaS-FFN layer: per-cube token selection, then the FFN of the
 active and text tokens plus mean compensation of the skipped ones; "value" is
 6 * hidden * inter * (active + text tokens) FLOPs per step time, and the
 roofline covers the adas_ffn_fwd call (its two GEMMs and the combine pass).
+
+With --backward (video workloads, cubes of 64 tokens) a step is one
+fine-tuning pass of the attention: partition, selection and the forward with
+its log-sum-exp, then the backward with the selection held fixed; "value" is
+(4 + 10) * d * (attended pairs) FLOPs per step time (forward: QK^T and PV;
+backward: S, dP, dV, dK and dQ), and the roofline covers the
+adas_sparse_attn_bwd call at 10 * d FLOPs per attended pair.
 """
 from __future__ import annotations
 
@@ -60,6 +67,8 @@ def parse():
                          "control: fixed budget versus the adaptive one)")
     ap.add_argument("--decode-batch", type=int, default=1,
                     help="decode tokens per step for the decode workload (1 = one step)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward of the sparse attention (selection held fixed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -133,6 +142,25 @@ def traffic_entry(workload: str):
     except Exception:
         return None
     if not rec or rec.get("attn_sources_sha256_16") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+BWD_SOURCES = ("attn_bwd.hip", "attn_bwd.h", "common.h")
+BWD_KERNELS = ["adas::k_bwd_prep<{d}>", "adas::k_bwd_dq<{d}>", "adas::k_bwd_lists", "adas::k_bwd_dkdv<{d}>"]
+
+
+def bwd_traffic_entry(workload: str):
+    """HBM bytes of one adas_sparse_attn_bwd call from rocprofv3 counters, if
+    the committed measurement is for the current backward sources."""
+    path = os.path.join(ROOT, "profiles", "bwd_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except Exception:
+        return None
+    if not rec or rec.get("bwd_sources_sha256_16") != source_hash_of(BWD_SOURCES):
         return None
     return rec.get("bytes_per_launch")
 
@@ -225,6 +253,119 @@ def cpu_baseline(wl, data, budget_s: float, topk: int = 0):
                       f"per row, float64 NumPy, 1 BLAS thread) in {t_rows:.1f} s; whole-input "
                       f"partition + mean keys took {t_layout:.1f} s and are not in the rate",
             "host_threads_available": len(os.sched_getaffinity(0))}
+
+
+def bwd_cpu_baseline(wl, data, budget_s: float):
+    """Time the CPU oracle on random video rows of the workload: selection
+    softmax, Top-p, then the row's attention and its gradients (float64 NumPy,
+    one BLAS thread)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import adas_oracle as O
+    from oracle import grad_oracle as G
+    rng = np.random.default_rng(321)
+    g = O.Geometry.of(wl)
+    rep = wl.n_q_heads // wl.n_kv_heads
+    flops, rows, t = 0.0, 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k_cube, _ = O.partition(data["k"], g)
+        v_cube, _ = O.partition(data["v"], g)
+        q_cube = O.partition(data["q"], g)[0]
+        kbar = O.mean_keys(k_cube, g)
+        t_layout = time.perf_counter() - t0
+        while t < budget_s:
+            hq, pos = int(rng.integers(wl.n_q_heads)), int(rng.integers(g.N))
+            kv, c = hq // rep, pos // g.S
+            do = rng.standard_normal(wl.head_dim)
+            t1 = time.perf_counter()
+            qv = O.to_f64(q_cube[hq, pos])
+            sel = O.top_p(O.selection_probabilities(qv, kbar[kv][:c]), wl.p)
+            cubes = sorted(set(int(j) for j in sel) | {c})
+            idx = np.concatenate([np.arange(j * g.S, (j + 1) * g.S) for j in cubes])
+            G.attend_grad(qv, O.to_f64(k_cube[kv][idx]), O.to_f64(v_cube[kv][idx]), do)
+            t += time.perf_counter() - t1
+            flops += 14.0 * wl.head_dim * len(idx)
+            rows += 1
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} random video rows of {wl.name} (selection softmax, Top-p, attention and its "
+                      f"gradients per row, float64 NumPy, 1 BLAS thread) in {t:.1f} s; whole-input partition "
+                      f"+ mean keys took {t_layout:.1f} s and are not in the rate",
+            "host_threads_available": len(os.sched_getaffinity(0))}
+
+
+def bwd_main(args):
+    import torch
+    import workloads
+    from adaptive_cube_sparse_amd import AdasAttentionGrad, Geometry
+
+    wl = workloads.get(args.config)
+    if not wl.video_queries or wl.dtype != "bf16" or wl.cube_size != 64 or wl.n_text or wl.n_decode:
+        print(f"--backward needs a bf16 video workload with cubes of 64 tokens and no extra rows "
+              f"(got {wl.name})", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    data = workloads.generate(wl)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    geom = Geometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw, wl.n_q_heads, wl.n_kv_heads, wl.head_dim)
+    layer = AdasAttentionGrad(geom, wl.p, has_video=True, n_extra=0, device=dev)
+    q, k, v = up(data["q"]), up(data["k"]), up(data["v"])
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+    dout = torch.randn((wl.n_tokens, wl.n_q_heads, wl.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    ev = {"forward": [], "backward": []}
+
+    def step(record):
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+        e0 = mark() if record else None
+        layer.forward(q, k, v)
+        e1 = mark() if record else None
+        layer.backward(dout)
+        e2 = mark() if record else None
+        if record:
+            ev["forward"].append((e0, e1))
+            ev["backward"].append((e1, e2))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in p])) for n, p in ev.items()}
+    pairs = attended_pairs(layer.fwd, wl)
+    d = wl.head_dim
+    value = 14.0 * d * pairs / (ms_step * 1e-3) / 1e12
+    bwd_flops = 10.0 * d * pairs
+    achieved = bwd_flops / (k_ms["backward"] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": bwd_traffic_entry(wl.name),
+            "algorithmic_flops_per_launch": bwd_flops,
+            "kernels": [k.format(d=d) for k in BWD_KERNELS], "launch_ms": k_ms["backward"]}
+    cpu = None if args.no_cpu_baseline else bwd_cpu_baseline(wl, data, args.cpu_seconds)
+    out = {
+        "metric": "AdaS-Attn forward + backward effective TFLOP/s (selected tokens, selection held fixed) "
+                  "and % of MI355X bf16 peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_bwd", "grid": [wl.T, wl.H, wl.W], "cube_thw": [wl.ct, wl.ch, wl.cw],
+                   "heads": [wl.n_q_heads, wl.n_kv_heads], "head_dim": d, "p": wl.p,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_ms": k_ms,
+        "attended_pairs": pairs,
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+    }
+    print(json.dumps(out), flush=True)
 
 
 FFN_METRIC = "AdaS-FFN effective TFLOP/s (active + text tokens) and % of MI355X bf16 peak"
@@ -345,6 +486,8 @@ def main():
     import workloads
     if args.config in workloads.FFN_WORKLOADS:
         return ffn_main(args)
+    if args.backward:
+        return bwd_main(args)
     from adaptive_cube_sparse_amd import AdasAttention, Geometry
 
     wl = workloads.get(args.config)

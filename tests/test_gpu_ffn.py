@@ -6,17 +6,19 @@ Bars:
     sides take the decision in float64 from the same bf16 bits; a row may
     differ only if the oracle's running sum at the cut lies within 1e-12 of p
     (counted; none expected).
-  * outputs: y is bf16.  Its error against float64 scales with the size of
-    the token's output row, not of the single element (FFN(x) may nearly
-    cancel x in one element): the final rounding of y (at most 2^-9 |y|, and
-    |y| reaches 4-5 rms(y) in a row of ~Gaussian entries: <= 9.8e-3 rms);
-    the bf16 rounding of the hidden activation before W_down (relative 2^-9
-    per element with independent signs, so about 2^-9/sqrt(3) = 1.1e-3
-    rms(FFN) per output, <= 6.8e-3 rms at 6 sigma); float32 accumulation
-    (~1e-6, negligible).  With
-    e = |y_dev - y_ref| / max(1, rms of the token's y_ref row) the bars are
-    max e <= 2e-2 (the two extremes added: 1.66e-2) and mean e <= 2e-3
-    (mean rounding 2^-11 |y| ~ 0.4e-3 plus mean H error 0.9e-3).
+  * outputs: y is bf16, whose unit roundoff is u = 2^-8 (8 significant
+    bits).  Its error against float64 scales with the size of the token's
+    output row, not of the single element (FFN(x) may nearly cancel x in one
+    element): the final rounding of y (at most u |y|, and |y| reaches 4-5
+    rms(y) in a row of ~Gaussian entries: <= 1.95e-2 rms); the bf16 rounding
+    of the hidden activation before W_down (relative error up to u per
+    element with independent signs, so about u/sqrt(3) = 2.3e-3 rms(FFN) per
+    output, <= 1.35e-2 rms at 6 sigma); float32 accumulation (~1e-6,
+    negligible).  Both extremes in one element are not expected together.
+    With e = |y_dev - y_ref| / max(1, rms of the token's y_ref row) the bars
+    are max e <= 3e-2 and mean e <= 3e-3 (mean final rounding about
+    u/4 E|y| / rms ~ 0.8e-3 to 1.1e-3, plus mean hidden-rounding error
+    0.8 u/sqrt(3) ~ 1.8e-3).
 """
 import math
 
@@ -31,7 +33,7 @@ from tests.gpu_harness import bits, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL_MAX, TOL_MEAN = 2e-2, 2e-3
+TOL_MAX, TOL_MEAN = 3e-2, 3e-3
 
 
 def _geom(wl):
