@@ -62,6 +62,14 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host-side stub was not emitted (clang drops it silently
+    # when a device builtin in its body fails the host pass) links fine and
+    # only fails when the library is loaded: refuse such a build here
+    nm = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True)
+    missing = [ln.strip() for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernels without host stubs (undefined symbols):\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

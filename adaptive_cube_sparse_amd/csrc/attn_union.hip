@@ -10,14 +10,18 @@
 // the own cube, or the causal text keys), one key block of 64 keys at a time:
 //   * K rows and V^T rows (values arrive cube-transposed, ADAS_LAYOUT_VT) of a
 //     block are staged in LDS.  When every block is full (S a multiple of 64)
-//     video blocks move global -> LDS with global_load_lds_dwordx4, two blocks
-//     ahead over three buffers; otherwise, and for text keys, through
-//     registers one block ahead.  Either way one barrier per block;
+//     video blocks move global -> LDS with buffer_load_dwordx4 ... lds over
+//     four buffers, two blocks ahead, one barrier per pair of blocks;
+//     otherwise, and for text keys, through registers one block ahead with
+//     one barrier per block;
 //   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, applies a
 //     per-row selection bit (row x cube bitmap built from the selection lists)
 //     as a +inf softmax bias, keeps the online softmax in log2 units with lazy
-//     rescaling, and accumulates O^T += V^T P^T.  A wave none of whose rows
-//     selected the cube skips the block.
+//     rescaling, and accumulates O^T += V^T P^T.  On full blocks the softmax
+//     unit is half a block (32 keys) and the units are software-pipelined:
+//     the exp / convert instructions of one unit are issued between the
+//     MFMAs of its neighbours.  A wave none of whose rows selected a pair of
+//     blocks skips the pair.
 // Rows spend MFMA work on every key block of the tile union; the masked part is
 // the price of keeping accumulators in registers.
 //
@@ -47,6 +51,21 @@ constexpr float kLazy = 8.0f;  // rescale only when a block max exceeds the refe
 constexpr float kOver = 16777216.0f;  // 2^24: largest block sum accepted without a block max
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+// 16 bytes per lane from base + voff + soff (a buffer of `bytes` bytes; reads
+// past it return 0) into LDS at lds + 16 * lane (lds wave-uniform)
+__device__ __forceinline__ void buffer_load_lds16(void* base, int bytes, void* lds, uint32_t voff, uint32_t soff) {
+  typedef __attribute__((address_space(3))) void lds_t;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 16, voff, soff, 0, 0);
+}
+// f(integral_constant<int, I>), ..., f(integral_constant<int, N - 1>)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 }  // namespace
 
 int union_tile_rows() { return UTR; }
@@ -355,6 +374,140 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using kFull = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
 
+  // ---- software-pipelined full blocks (video walks when FULL) ---------------------------
+  // The softmax unit is a half block of 32 keys; unit u of a call is half u % 2
+  // of block u / 2.  S(u): its score MFMAs; sm(u): its softmax on the vector
+  // ALUs; PV(u): its MFMAs into the output (D/16 each).  The units of one or two blocks
+  // run as steps S(0); S(1)|sm(0); S(2) PV(0)|sm(1); S(3) PV(1)|sm(2);
+  // PV(2)|sm(3); PV(3).  Within a step the order is fixed by scheduling
+  // barriers: slot k issues the LDS operand read of MFMA k+2, MFMA k, then a
+  // slice of the softmax, so the exp and convert instructions of one unit run
+  // while the MFMAs of its neighbours execute.  Scores and probabilities
+  // alternate between two register slots (u % 2); S and PV MFMAs of a step
+  // alternate, so consecutive MFMAs use different accumulators.
+  f32x16 su[2];
+  bf16x8u pu[2][2];
+  auto run_step = [&](auto sUc, auto pvUc, auto smUc, const uint16_t* kb, const uint16_t* vb,
+                      bool sel) __attribute__((always_inline)) {
+    constexpr int sU = decltype(sUc)::value, pvU = decltype(pvUc)::value, smU = decltype(smUc)::value;
+    constexpr bool HS = sU >= 0, HP = pvU >= 0, HM = smU >= 0;
+    constexpr int NO = D / 16;  // MFMAs of one S(u) (k-steps over d) and of one PV(u) (2 k-steps x D/32 tiles)
+    constexpr int ND = D / 32;
+    constexpr int NM = (HS ? NO : 0) + (HP ? NO : 0);
+    constexpr int ss = sU & 1, ps = pvU & 1, ms = smU & 1;
+    uint4 f[3];
+    auto is_s = [](auto kc) constexpr { return HS && (!HP || (decltype(kc)::value % 2) == 0); };
+    auto op_i = [](auto kc) constexpr { return (HS && HP) ? decltype(kc)::value / 2 : decltype(kc)::value; };
+    auto rd = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, i = op_i(kc);
+      if constexpr (is_s(kc))
+        f[k % 3] = *reinterpret_cast<const uint4*>(&kb[(32 * ss + lr) * Sm::KS + 16 * i + 8 * lh]);
+      else
+        f[k % 3] = *reinterpret_cast<const uint4*>(&vb[(32 * (i % ND) + lr) * Sm::VS + 16 * (2 * ps + i / ND) + 8 * lh]);
+    };
+    auto mf = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, i = op_i(kc);
+      const bf16x8u a8 = __builtin_bit_cast(bf16x8u, f[k % 3]);
+      if constexpr (is_s(kc)) {
+        if constexpr (i == 0) {
+          const f32x16 z = {};
+          su[ss] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, qb[0], z, 0, 0, 0);
+        } else {
+          su[ss] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, qb[i], su[ss], 0, 0, 0);
+        }
+      } else {
+        acc[i % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pu[ps][i / ND], acc[i % ND], 0, 0, 0);
+      }
+    };
+    // softmax of unit smU in 8 pieces (pairs of exp / convert / row-sum),
+    // against the row's current reference m_run with no unit max: while
+    // every selected row has a reference and its unit sum stays below kOver,
+    // that is exact.  Otherwise (a row's first unit, or a unit far above the
+    // reference) the slow path after the step takes the unit max, raises the
+    // reference lazily (only past 2^kLazy), rescales and forms P again.
+    const float bias = sel ? m_run : INFINITY;
+    float ls = 0.f;
+    auto piece = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int e = decltype(ic)::value;
+      const __bf16 p0 = (__bf16)ex2(fmaf(su[ms][2 * e], qscale, -bias));
+      const __bf16 p1 = (__bf16)ex2(fmaf(su[ms][2 * e + 1], qscale, -bias));
+      pu[ms][e / 4][2 * (e % 4)] = p0;
+      pu[ms][e / 4][2 * (e % 4) + 1] = p1;
+      const bf16x2u pair = {p0, p1};
+      ls = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ls, false);
+    };
+    if constexpr (NM > 0) rd(std::integral_constant<int, 0>{});
+    if constexpr (NM > 1) rd(std::integral_constant<int, 1>{});
+    static_for<0, NM>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k + 2 < NM) rd(std::integral_constant<int, k + 2>{});
+      mf(kc);
+      if constexpr (HM)
+        static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
+          if constexpr ((decltype(ic)::value * NM) / 8 == k) piece(ic);
+        });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (HM) {
+      float lsu = ls + xor32_f32(ls);
+      if (__ballot(sel && (m_run == -INFINITY || !(lsu <= kOver))) != 0ull) {
+        float mb = fmaxf(su[ms][0], su[ms][1]);
+#pragma unroll
+        for (int e = 2; e < 16; e += 2) mb = fmaxf(fmaxf(mb, su[ms][e]), su[ms][e + 1]);
+        mb = fmaxf(mb, xor32_f32(mb));
+        const float mb_c = sel ? mb * qscale : -INFINITY;
+        const bool grow = mb_c > m_run + kLazy;
+        // the accumulators already hold PV(smU - 1), formed against the old
+        // reference, so rescaling them here is exact
+        if (__ballot(grow) != 0ull) {
+          const float alpha = grow ? ex2(m_run - mb_c) : 1.0f;  // 0 when m_run = -inf
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+          m_run = grow ? mb_c : m_run;
+        }
+        const float b2 = (sel && m_run != -INFINITY) ? m_run : INFINITY;
+        float l2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 p0 = (__bf16)ex2(fmaf(su[ms][2 * e], qscale, -b2));
+          const __bf16 p1 = (__bf16)ex2(fmaf(su[ms][2 * e + 1], qscale, -b2));
+          pu[ms][e / 4][2 * (e % 4)] = p0;
+          pu[ms][e / 4][2 * (e % 4) + 1] = p1;
+          const bf16x2u pair = {p0, p1};
+          l2 = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l2, false);
+        }
+        lsu = l2 + xor32_f32(l2);
+      }
+      l_run += lsu;
+    }
+  };
+  using UN = std::integral_constant<int, -1>;
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
+  // one full block
+  auto block1 = [&](const uint16_t* kb, const uint16_t* vb, bool sel) __attribute__((always_inline)) {
+    run_step(U0{}, UN{}, UN{}, kb, vb, sel);
+    run_step(U1{}, UN{}, U0{}, kb, vb, sel);
+    run_step(UN{}, U0{}, U1{}, kb, vb, sel);
+    run_step(UN{}, U1{}, UN{}, kb, vb, sel);
+  };
+  // two full blocks
+  auto block2 = [&](const uint16_t* kb0, const uint16_t* vb0, bool sel0, const uint16_t* kb1,
+                    const uint16_t* vb1, bool sel1) __attribute__((always_inline)) {
+    run_step(U0{}, UN{}, UN{}, kb0, vb0, sel0);
+    run_step(U1{}, UN{}, U0{}, kb0, vb0, sel0);
+    run_step(U2{}, U0{}, U1{}, kb1, vb0, sel0);
+    run_step(U3{}, U1{}, U2{}, kb1, vb0, sel1);
+    run_step(UN{}, U2{}, U3{}, kb1, vb1, sel1);
+    run_step(UN{}, U3{}, UN{}, kb1, vb1, sel1);
+  };
+
   // Register-staged walk over nb key blocks: source(i, kptr, vptr, stride, kc)
   // names block i (vt: values cube-transposed), work(i, buf, kc) computes it.
   // One barrier per block: staging into buffer i&1 is safe because every
@@ -421,22 +574,26 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   typedef __attribute__((address_space(3))) void lds_void;
   // issue this wave's loads of the block whose K rows start at kb and whose
   // V^T rows start at vb (bytes), into buffer buf
-  auto issue = [&](const char* kb, const char* vb, auto bufc) __attribute__((always_inline)) {
+  // Buffer loads (MUBUF) rather than global_load_lds: the compiler's wait
+  // counting treats a pending FLAT load into LDS as an LDS access too and then
+  // answers every LDS operand read with lgkmcnt(0), draining the reads issued
+  // ahead of the MFMAs; a buffer load is counted on vmcnt only.  One
+  // descriptor per KV head's K rows and V^T rows; ko / vo are the block's byte
+  // offsets inside them.
+  const int head_bytes = (int)((size_t)g.NS * D * 2);  // < 2^31 (checked at launch)
+  void* const kbase = (void*)((const uint16_t*)a.k_cube + (size_t)grp * g.NS * D);
+  void* const vbase = (void*)((const uint16_t*)a.v_cube + (size_t)grp * g.NS * D);
+  auto issue = [&](uint32_t ko, uint32_t vo, auto bufc) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NLW; ++m) {
       if (dok[m]) {
         if (disk[m])
-          __builtin_amdgcn_global_load_lds((const void*)(kb + dsrc[m]),
-                                           (lds_void*)((char*)kbuf_c(bufc) + dlds[m]), 16, 0, 0);
+          buffer_load_lds16(kbase, head_bytes, (char*)kbuf_c(bufc) + dlds[m], dsrc[m], ko);
         else
-          __builtin_amdgcn_global_load_lds((const void*)(vb + dsrc[m]),
-                                           (lds_void*)((char*)vbuf_c(bufc) + dlds[m]), 16, 0, 0);
+          buffer_load_lds16(vbase, head_bytes, (char*)vbuf_c(bufc) + dlds[m], dsrc[m], vo);
       }
     }
   };
-  // Three buffers, loads two blocks ahead, one barrier per block.  Block i+2
-  // goes to buffer (i+2)%3, last read by block i-1, which every wave finished
-  // before the barrier of block i.
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
@@ -451,9 +608,9 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     __syncthreads();  // the previous phase no longer reads any buffer
     auto issue_block = [&](int i, auto bufc) __attribute__((always_inline)) {
       if (i < nb) {
-        const char *kb, *vb;
-        bsrc(i, kb, vb);
-        issue(kb, vb, bufc);
+        uint32_t ko, vo;
+        bsrc(i, ko, vo);
+        issue(ko, vo, bufc);
       }
     };
     issue_block(0, C0{});
@@ -469,8 +626,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         issue_block(i + 2, n0);
         issue_block(i + 3, n1);
       }
-      work(i, kbuf_c(b0), vbuf_c(b0), UKB);
-      if (i + 1 < nb) work(i + 1, kbuf_c(b1), vbuf_c(b1), UKB);
+      work(i, kbuf_c(b0), vbuf_c(b0), kbuf_c(b1), vbuf_c(b1), i + 1 < nb);
     };
     for (int i = 0; i < nb; i += 4) {
       pair(C0{}, C1{}, C2{}, C3{}, i);
@@ -484,18 +640,19 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.NS * D;  // [Nc][D][S] (ADAS_LAYOUT_VT)
 
   // ---- own cube (video): every row ------------------------------------------------------
-  const char* vtg = (const char*)a.v_cube + (size_t)grp * g.NS * D * 2;  // [Nc][D][S] per group
   if (video) {
     if constexpr (FULL) {
       dpipeline(
           nkb_cube,
-          [&](int i, const char*& kb, const char*& vb) __attribute__((always_inline)) {
-            kb = (const char*)(kg + ((size_t)c * g.S + i * UKB) * D);
-            vb = vtg + (size_t)c * g.S * D * 2 + i * UKB * 2;
+          [&](int i, uint32_t& ko, uint32_t& vo) __attribute__((always_inline)) {
+            ko = (uint32_t)(((size_t)c * g.S + i * UKB) * D * 2);
+            vo = (uint32_t)((size_t)c * g.S * D * 2 + i * UKB * 2);
           },
-          [&](int, const uint16_t* kb_, const uint16_t* vb_, int kc) __attribute__((always_inline)) {
+          [&](int, const uint16_t* kb0, const uint16_t* vb0, const uint16_t* kb1, const uint16_t* vb1,
+              bool two) __attribute__((always_inline)) {
             if (!wave_has_rows) return;
-            compute(kFull{}, kb_, vb_, row_ok, kc, false, 0);
+            if (two) block2(kb0, vb0, row_ok, kb1, vb1, row_ok);
+            else block1(kb0, vb0, row_ok);
           });
     } else {
     pipeline(
@@ -606,23 +763,28 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     __syncthreads();
     if constexpr (FULL) {
       const int nblk = s_nunion * nkb_cube;
-      uint32_t mw_next = nblk > 0 ? s_bits[UNW * s_ulist[0] + wave] : 0u;
       dpipeline(
           nblk,
-          [&](int i, const char*& kb, const char*& vb) __attribute__((always_inline)) {
+          [&](int i, uint32_t& ko, uint32_t& vo) __attribute__((always_inline)) {
             const int ci = i / nkb_cube, kbi = i - ci * nkb_cube;
             const int j = __builtin_amdgcn_readfirstlane(jb + s_ulist[ci]);
-            kb = (const char*)(kg + ((size_t)j * g.S + kbi * UKB) * D);
-            vb = vtg + (size_t)j * g.S * D * 2 + kbi * UKB * 2;
+            ko = (uint32_t)(((size_t)j * g.S + kbi * UKB) * D * 2);
+            vo = (uint32_t)((size_t)j * g.S * D * 2 + kbi * UKB * 2);
           },
-          [&](int i, const uint16_t* kb_, const uint16_t* vb_, int kc) __attribute__((always_inline)) {
-            // this wave's row mask of block i was read one block earlier; the
-            // read for block i+1 overlaps this block
-            const uint32_t mw = mw_next;
-            if (i + 1 < nblk) mw_next = s_bits[UNW * s_ulist[(i + 1) / nkb_cube] + wave];
-            if (mw == 0u) return;
-            const bool sel = ((mw >> lr) & 1u) != 0u;
-            compute(kFull{}, kb_, vb_, sel, kc, false, 0);
+          [&](int i, const uint16_t* kb0, const uint16_t* vb0, const uint16_t* kb1, const uint16_t* vb1,
+              bool two) __attribute__((always_inline)) {
+            // this wave's row masks of blocks i and i+1; a block none of the
+            // wave's rows selected is skipped
+            const uint32_t mw0 = s_bits[UNW * s_ulist[i / nkb_cube] + wave];
+            const uint32_t mw1 = two ? s_bits[UNW * s_ulist[(i + 1) / nkb_cube] + wave] : 0u;
+            const bool sel0 = ((mw0 >> lr) & 1u) != 0u, sel1 = ((mw1 >> lr) & 1u) != 0u;
+            // a block none of the wave's rows selected (rare in union tiles)
+            // runs with every row masked rather than splitting the paths
+            if (two) {
+              if ((mw0 | mw1) != 0u) block2(kb0, vb0, sel0, kb1, vb1, sel1);
+            } else if (mw0 != 0u) {
+              block1(kb0, vb0, sel0);
+            }
           });
     } else {
     pipeline(
@@ -708,6 +870,8 @@ hipError_t launch_union(const AttnArgs& a, hipStream_t s) {
     }
   }
   const long blocks = sc.n_extra_wgs + video_blocks;
+  // buffer descriptors address one KV head's K (or V^T) rows with 32-bit offsets
+  if ((size_t)a.g.NS * D * 2 > 0x7fffffffu) return hipErrorInvalidValue;
   if (blocks > 0) {
     if (a.g.S % UKB == 0)
       hipLaunchKernelGGL((k_attn_union<D, true>), dim3((unsigned)blocks), dim3(UNT), 0, s, a, sc);
