@@ -247,23 +247,24 @@ __global__ __launch_bounds__(BNT, 1) void k_bwd_dq(BwdArgs a) {
     }
     dlds[m] = q * 1024;
   }
-  typedef __attribute__((address_space(3))) void lds_void;
-  const char* kgp = (const char*)(a.k_cube + (size_t)grp * g.NS * D);
-  const char* vgp = (const char*)(a.v_tok + (size_t)grp * g.NS * D);
-  const char* tgp = (const char*)(a.k_vt + (size_t)grp * g.NS * D);
+  // buffer loads into LDS (counted on vmcnt only; see buffer_load_lds16), one
+  // descriptor per KV head's K rows, V rows and K^T rows
+  const int head_bytes = (int)((size_t)g.NS * D * 2);  // < 2^31 (checked at launch)
+  void* const kgp = (void*)(a.k_cube + (size_t)grp * g.NS * D);
+  void* const vgp = (void*)(a.v_tok + (size_t)grp * g.NS * D);
+  void* const tgp = (void*)(a.k_vt + (size_t)grp * g.NS * D);
   // block i of a walk: cube j, key block kbi
   auto issue = [&](int j, int kbi, auto bufc) __attribute__((always_inline)) {
-    const char* kb = kgp + ((size_t)j * g.S + kbi * BKB) * D * 2;
-    const char* vb = vgp + ((size_t)j * g.S + kbi * BKB) * D * 2;
-    const char* tb = tgp + (size_t)j * g.S * D * 2 + kbi * BKB * 2;
+    const uint32_t kvo = (uint32_t)(((size_t)j * g.S + kbi * BKB) * D * 2);
+    const uint32_t to = (uint32_t)((size_t)j * g.S * D * 2 + kbi * BKB * 2);
 #pragma unroll
     for (int m = 0; m < NLW; ++m) {
       if (dkind[m] == 0)
-        __builtin_amdgcn_global_load_lds((const void*)(kb + dsrc[m]), (lds_void*)((char*)kbuf(bufc) + dlds[m]), 16, 0, 0);
+        buffer_load_lds16(kgp, head_bytes, (char*)kbuf(bufc) + dlds[m], dsrc[m], kvo);
       else if (dkind[m] == 1)
-        __builtin_amdgcn_global_load_lds((const void*)(vb + dsrc[m]), (lds_void*)((char*)vbuf(bufc) + dlds[m]), 16, 0, 0);
+        buffer_load_lds16(vgp, head_bytes, (char*)vbuf(bufc) + dlds[m], dsrc[m], kvo);
       else if (dkind[m] == 2)
-        __builtin_amdgcn_global_load_lds((const void*)(tb + dsrc[m]), (lds_void*)((char*)tbuf(bufc) + dlds[m]), 16, 0, 0);
+        buffer_load_lds16(tgp, head_bytes, (char*)tbuf(bufc) + dlds[m], dsrc[m], to);
     }
   };
   using C0 = std::integral_constant<int, 0>;
@@ -667,6 +668,8 @@ void bind_backward_workspace(BwdArgs& a, void* ws) {
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   const KGeom& g = a.g;
+  // buffer descriptors address one KV head's rows with 32-bit offsets
+  if ((size_t)g.NS * g.D * 2 > 0x7fffffffu) return hipErrorInvalidValue;
   const int rows = g.Hq * a.rows_per_head;
   const int nkb = g.S / BKB;
   if (g.D == 128) {

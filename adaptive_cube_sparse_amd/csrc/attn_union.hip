@@ -51,13 +51,6 @@ constexpr float kLazy = 8.0f;  // rescale only when a block max exceeds the refe
 constexpr float kOver = 16777216.0f;  // 2^24: largest block sum accepted without a block max
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-// 16 bytes per lane from base + voff + soff (a buffer of `bytes` bytes; reads
-// past it return 0) into LDS at lds + 16 * lane (lds wave-uniform)
-__device__ __forceinline__ void buffer_load_lds16(void* base, int bytes, void* lds, uint32_t voff, uint32_t soff) {
-  typedef __attribute__((address_space(3))) void lds_t;
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 16, voff, soff, 0, 0);
-}
 // f(integral_constant<int, I>), ..., f(integral_constant<int, N - 1>)
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -574,12 +567,8 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   typedef __attribute__((address_space(3))) void lds_void;
   // issue this wave's loads of the block whose K rows start at kb and whose
   // V^T rows start at vb (bytes), into buffer buf
-  // Buffer loads (MUBUF) rather than global_load_lds: the compiler's wait
-  // counting treats a pending FLAT load into LDS as an LDS access too and then
-  // answers every LDS operand read with lgkmcnt(0), draining the reads issued
-  // ahead of the MFMAs; a buffer load is counted on vmcnt only.  One
-  // descriptor per KV head's K rows and V^T rows; ko / vo are the block's byte
-  // offsets inside them.
+  // Buffer loads into LDS (buffer_load_lds16), one descriptor per KV head's K
+  // rows and V^T rows; ko / vo are the block's byte offsets inside them.
   const int head_bytes = (int)((size_t)g.NS * D * 2);  // < 2^31 (checked at launch)
   void* const kbase = (void*)((const uint16_t*)a.k_cube + (size_t)grp * g.NS * D);
   void* const vbase = (void*)((const uint16_t*)a.v_cube + (size_t)grp * g.NS * D);

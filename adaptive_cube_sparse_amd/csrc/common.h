@@ -117,6 +117,19 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// 16 bytes per lane from base + voff + soff (a buffer of `bytes` bytes; reads
+// past it return 0) into LDS at lds + 16 * lane (lds wave-uniform).  A buffer
+// load (MUBUF) rather than global_load_lds: the compiler counts a pending FLAT
+// load into LDS as an LDS access too and then answers every LDS operand read
+// with lgkmcnt(0); a buffer load is counted on vmcnt only.  Kept out of
+// lambdas: inside one, the builtin fails the host pass silently and the
+// enclosing kernel loses its host stub.
+__device__ __forceinline__ void buffer_load_lds16(void* base, int bytes, void* lds, uint32_t voff, uint32_t soff) {
+  typedef __attribute__((address_space(3))) void lds_t;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp(float x) {
   // exp(x) = 2^(x*log2 e); v_exp_f32 is accurate to ~1 ulp on normal results.
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);

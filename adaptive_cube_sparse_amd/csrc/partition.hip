@@ -42,46 +42,87 @@ __global__ __launch_bounds__(256) void k_partition(const uint4* __restrict__ src
 }
 
 // ADAS_LAYOUT_VT: one workgroup per (cube, head) stages up to 64 offsets x d
-// in LDS (rows padded by one 32-bit word against bank conflicts), then writes
-// each d-row of the transposed cube: position p of row e takes offset
-// vt_column(p), so consecutive threads write consecutive positions.
+// in LDS, then writes each d-row of the transposed cube: position p of row e
+// takes offset vt_column(p).  Both sides move 16 bytes per thread: a load is
+// one token's 16-byte piece of d (written to LDS as 4-byte words, rows padded
+// to an odd word count, so the gathers below do not collide on banks); a
+// store is EPV consecutive positions of one d-row, gathered from LDS.  A
+// store whose positions straddle the frame window is done element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void k_partition_vt(const T* __restrict__ src, T* __restrict__ dst,
                                                       int32_t* __restrict__ perm, KGeom g, int nh,
                                                       int f_lo, int f_hi, int c_lo) {
-  constexpr int PAD = 4 / (int)sizeof(T);
-  __shared__ T tile[64 * (128 + PAD)];
+  constexpr int EPV = 16 / (int)sizeof(T);   // elements per 16-byte vector
+  constexpr int WPT = (int)sizeof(T) == 2 ? 2 : 1;  // elements per 4-byte LDS word
+  constexpr int TS = 128 / WPT + 1;          // LDS row stride in words (d <= 128)
+  __shared__ uint32_t tile[64 * TS];
   const int c = c_lo + blockIdx.x;
   const int h = blockIdx.y;
   const int bx = c % g.nW;
   const int by = (c / g.nW) % g.nH;
   const int bt = c / (g.nW * g.nH);
   const int hw = g.ch * g.cw;
-  const int D = g.D, TS = g.D + PAD;
+  const int D = g.D;
+  const int VPR = D / EPV;  // 16-byte vectors per token row
   T* out = dst + ((size_t)h * (g.NS / g.S) + c) * (size_t)D * g.S;
+  auto in_window = [&](int r) { const int f = bt * g.ct + r / hw; return f >= f_lo && f < f_hi; };
   for (int r0 = 0; r0 < g.S; r0 += 64) {
     const int nk = min(64, g.S - r0);
     __syncthreads();  // the previous chunk's reads of `tile` are done
-    for (int e = threadIdx.x; e < nk * D; e += blockDim.x) {
-      const int rr = e / D, col = e - rr * D;
+    for (int e = threadIdx.x; e < nk * VPR; e += blockDim.x) {
+      const int rr = e / VPR, v = e - rr * VPR;
       const int r = r0 + rr;
+      if (!in_window(r)) continue;
       const int dt = r / hw;
       const int rem = r - dt * hw;
       const int dy = rem / g.cw;
       const int dx = rem - dy * g.cw;
       const int f = bt * g.ct + dt;
-      if (f < f_lo || f >= f_hi) continue;
       const int n = ((f - f_lo) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
-      tile[rr * TS + col] = src[((size_t)n * nh + h) * D + col];
-      if (perm != nullptr && h == 0 && col == 0) perm[c * g.S + r] = n;
+      const uint4 x = *reinterpret_cast<const uint4*>(src + ((size_t)n * nh + h) * D + v * EPV);
+      uint32_t* t = &tile[rr * TS + v * (EPV / WPT)];
+      t[0] = x.x;
+      t[1] = x.y;
+      t[2] = x.z;
+      t[3] = x.w;
+      if (perm != nullptr && h == 0 && v == 0) perm[c * g.S + r] = n;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < nk * D; e += blockDim.x) {
-      const int d = e / nk, pl = e - d * nk;
-      const int r = vt_column(r0 + pl, g.S);  // groups of 16 never straddle r0
-      const int f = bt * g.ct + r / hw;
-      if (f < f_lo || f >= f_hi) continue;
-      out[(size_t)d * g.S + r0 + pl] = tile[(r - r0) * TS + d];
+    if (g.S % EPV != 0) {
+      // rows not 16-byte aligned: one element per thread
+      for (int e = threadIdx.x; e < nk * D; e += blockDim.x) {
+        const int d = e / nk, pl = e - d * nk;
+        const int r = vt_column(r0 + pl, g.S);
+        if (!in_window(r)) continue;
+        const uint32_t w = tile[(r - r0) * TS + d / WPT];
+        out[(size_t)d * g.S + r0 + pl] = (T)(WPT == 2 ? ((d & 1) ? (w >> 16) : (w & 0xFFFFu)) : w);
+      }
+      continue;
+    }
+    const int GPR = nk / EPV;  // 16-byte groups per d-row of the chunk
+    for (int e = threadIdx.x; e < D * GPR; e += blockDim.x) {
+      const int d = e / GPR, q = e - d * GPR;
+      T val[EPV];
+      bool all = true, any = false;
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) {
+        const int r = vt_column(r0 + EPV * q + i, g.S);  // groups of 16 never straddle r0
+        const bool ok = in_window(r);
+        all = all && ok;
+        any = any || ok;
+        const uint32_t w = tile[(r - r0) * TS + d / WPT];
+        val[i] = (T)(WPT == 2 ? ((d & 1) ? (w >> 16) : (w & 0xFFFFu)) : w);
+      }
+      T* o = out + (size_t)d * g.S + r0 + EPV * q;
+      if (all) {
+        uint4 v;
+        __builtin_memcpy(&v, val, 16);
+        *reinterpret_cast<uint4*>(o) = v;
+      } else if (any) {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i)
+          if (in_window(vt_column(r0 + EPV * q + i, g.S))) o[i] = val[i];
+      }
     }
   }
 }

@@ -1,0 +1,59 @@
+"""GPU cube partition in both layouts against the oracle's partition, bit for
+bit, through the C ABI (adas_cube_partition).
+
+ADAS_LAYOUT_TOKENS must equal the oracle's cube-contiguous copy and perm;
+ADAS_LAYOUT_VT must equal that copy transposed per cube with the column
+permutation include/adas.h states (bits 2 and 3 swapped inside complete aligned
+groups of 16 offsets).  The shapes cover 16-byte stores of 8 bf16 or 4 float32
+positions (S = 24, 32, 64, 128; S = 24 ends in a partial group of 8), the
+element-wise path for an S that is not a multiple of the vector width (S = 9),
+and a head count other than the attention's.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import adas_oracle as O
+from tests.gpu_harness import bits, log, to_vt
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # T, H, W, ct, ch, cw, dtype, d, heads
+    (4, 16, 16, 4, 4, 4, "bf16", 128, 2),
+    (8, 16, 16, 2, 8, 8, "bf16", 128, 3),
+    (4, 8, 8, 2, 4, 4, "f32", 64, 1),
+    (2, 12, 12, 2, 3, 4, "bf16", 128, 2),
+    (4, 6, 6, 1, 3, 3, "bf16", 64, 2),
+    (8, 16, 16, 2, 8, 8, "f32", 64, 2),
+    (2, 8, 8, 1, 2, 2, "f32", 128, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s[:6])) + f"_{s[6]}_d{s[7]}_h{s[8]}")
+def test_partition_layouts_bit_exact(shape):
+    from adaptive_cube_sparse_amd import ADAS_LAYOUT_VT, Geometry, adas_cube_partition
+    T, H, W, ct, ch, cw, dt, d, nh = shape
+    N, S = T * H * W, ct * ch * cw
+    log(f"[partition] grid {T}x{H}x{W} cube ({ct},{ch},{cw}) S {S} {dt} d {d} heads {nh}")
+    rng = np.random.default_rng(S * 1000 + d + nh)
+    if dt == "bf16":
+        raw = rng.integers(0, 1 << 16, size=(N, nh, d), dtype=np.uint16)
+        x = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    else:
+        raw = rng.integers(0, 1 << 32, size=(N, nh, d), dtype=np.uint32)
+        x = torch.from_numpy(raw.view(np.int32)).view(torch.float32).to("cuda:0")
+    geom = Geometry(T, H, W, ct, ch, cw, nh, nh, d)
+    tok = torch.empty((nh, N, d), dtype=x.dtype, device=x.device)
+    vt = torch.empty((nh, N // S, d, S), dtype=x.dtype, device=x.device)
+    perm = torch.empty((N,), dtype=torch.int32, device=x.device)
+    adas_cube_partition(geom, x, tok, perm)
+    adas_cube_partition(geom, x, vt, None, layout=ADAS_LAYOUT_VT)
+    torch.cuda.synchronize()
+    g = O.Geometry(T, H, W, ct, ch, cw)
+    want, want_perm = O.partition(raw, g)
+    got_tok = bits(tok) if dt == "bf16" else tok.cpu().view(torch.int32).numpy().view(np.uint32)
+    got_vt = bits(vt) if dt == "bf16" else vt.cpu().view(torch.int32).numpy().view(np.uint32)
+    assert np.array_equal(perm.cpu().numpy(), want_perm), "perm differs"
+    assert np.array_equal(got_tok, want), "token layout differs"
+    assert np.array_equal(got_vt, to_vt(want, S)), "VT layout differs"
