@@ -628,6 +628,23 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   const uint16_t* kg = (const uint16_t*)a.k_cube + (size_t)grp * g.NS * D;
   const uint16_t* vg = (const uint16_t*)a.v_cube + (size_t)grp * g.NS * D;  // [Nc][D][S] (ADAS_LAYOUT_VT)
 
+  if constexpr (FULL) {
+    // block buffers start zeroed, so a masked stand-in block reads finite values
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int e = tid; e < UKB * Sm::KS / 8; e += UNT) {
+      reinterpret_cast<uint4*>(lk0)[e] = z;
+      reinterpret_cast<uint4*>(lk1)[e] = z;
+      reinterpret_cast<uint4*>(lk2)[e] = z;
+      reinterpret_cast<uint4*>(lk3)[e] = z;
+    }
+    for (int e = tid; e < D * Sm::VS / 8; e += UNT) {
+      reinterpret_cast<uint4*>(lv0)[e] = z;
+      reinterpret_cast<uint4*>(lv1)[e] = z;
+      reinterpret_cast<uint4*>(lv2)[e] = z;
+      reinterpret_cast<uint4*>(lv3)[e] = z;
+    }
+  }
+
   // ---- own cube (video): every row ------------------------------------------------------
   if (video) {
     if constexpr (FULL) {
@@ -762,18 +779,16 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
           },
           [&](int i, const uint16_t* kb0, const uint16_t* vb0, const uint16_t* kb1, const uint16_t* vb1,
               bool two) __attribute__((always_inline)) {
-            // this wave's row masks of blocks i and i+1; a block none of the
-            // wave's rows selected is skipped
+            // this wave's row masks of blocks i and i+1.  Every pair runs the
+            // two-block path, with no skipping (in union tiles a wave whose 32
+            // rows all pass over a block is rare): one code path keeps the
+            // accumulators in place instead of copying them where paths meet.
+            // An odd last block pairs with the other buffer's stale (finite,
+            // zeroed at the start) contents, every row masked.
             const uint32_t mw0 = s_bits[UNW * s_ulist[i / nkb_cube] + wave];
             const uint32_t mw1 = two ? s_bits[UNW * s_ulist[(i + 1) / nkb_cube] + wave] : 0u;
             const bool sel0 = ((mw0 >> lr) & 1u) != 0u, sel1 = ((mw1 >> lr) & 1u) != 0u;
-            // a block none of the wave's rows selected (rare in union tiles)
-            // runs with every row masked rather than splitting the paths
-            if (two) {
-              if ((mw0 | mw1) != 0u) block2(kb0, vb0, sel0, kb1, vb1, sel1);
-            } else if (mw0 != 0u) {
-              block1(kb0, vb0, sel0);
-            }
+            block2(kb0, vb0, sel0, kb1, vb1, sel1);
           });
     } else {
     pipeline(
