@@ -243,7 +243,8 @@ static size_t bitmap_bytes(const AttnArgs& a) {
 size_t attention_workspace_bytes(const AttnArgs& a, adas_dtype dt) {
   if (dt != ADAS_BF16 || a.n_extra == 0) return 0;
   size_t bytes = bitmap_bytes(a);
-  if (a.extra_chunks > 1) {
+  // the decode kernel always leaves partial rows for k_merge_bf16, even with one chunk
+  if (a.extra_chunks > 1 || a.decode_chunks > 0) {
     const int TR = a.decode_chunks > 0 ? 32 : union_tile_rows();
     bytes += (size_t)a.g.Hkv * a.extra_tiles_per_group * a.extra_chunks * TR * (a.g.D + 2) * sizeof(float);
   }
@@ -255,7 +256,7 @@ void bind_attention_workspace(AttnArgs& a, adas_dtype dt, void* ws) {
   a.partials = nullptr;
   if (dt != ADAS_BF16 || a.n_extra == 0) return;
   a.extra_bits = (uint32_t*)ws;
-  if (a.extra_chunks > 1) a.partials = (float*)((char*)ws + bitmap_bytes(a));
+  if (a.extra_chunks > 1 || a.decode_chunks > 0) a.partials = (float*)((char*)ws + bitmap_bytes(a));
 }
 
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s) {

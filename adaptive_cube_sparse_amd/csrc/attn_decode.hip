@@ -7,8 +7,8 @@
 // same <= 32 rows (query operand and float32 accumulators in registers) and
 // walks its own cubes of the chunk (cube c0 + wave, + 4, ...), skipping cubes no
 // row selected.  Each wave owns one LDS block buffer: a key block (64 keys of
-// K rows and V^T rows, values in ADAS_LAYOUT_VT) arrives there by
-// global_load_lds_dwordx4 in 1 KB contiguous pieces, then feeds the MFMAs with
+// K rows and V^T rows, values in ADAS_LAYOUT_VT) arrives there by buffer
+// loads into LDS in 1 KB contiguous pieces, then feeds the MFMAs with
 // the same conflict-free b128 fragment reads as the union kernel.  Waves share
 // no data while they walk their cubes, so there is no barrier in the loop; the
 // four waves of a CU overlap one another's loads and math.  At the end the
@@ -78,11 +78,11 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint16_t* mk = lds_k[wv];
   uint16_t* mv = lds_v[wv];
-  typedef __attribute__((address_space(3))) void lds_void;
 
   const uint32_t* rbits = a.extra_bits + (size_t)(hq * a.n_extra + m) * a.bits_words;
-  const char* kg = (const char*)a.k_cube + (size_t)grp * g.NS * D * 2;
-  const char* vg = (const char*)a.v_cube + (size_t)grp * g.NS * D * 2;  // [Nc][D][S]
+  const int head_bytes = (int)((size_t)g.NS * D * 2);  // < 2^31 (checked at launch)
+  void* const kg = (void*)((const uint16_t*)a.k_cube + (size_t)grp * g.NS * D);
+  void* const vg = (void*)((const uint16_t*)a.v_cube + (size_t)grp * g.NS * D);  // [Nc][D][S]
   const int c0 = chunk * a.extra_chunk_cubes;
   const int c1 = min(g.Nc, c0 + a.extra_chunk_cubes);
   for (int j = c0 + wv; j < c1; j += DW) {
@@ -93,22 +93,20 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
     for (int kb = 0; kb < g.S; kb += 64) {
       // piece e = 64*q + lane of the padded block; the padding column re-reads
       // the row's first piece
-      const char* kblk = kg + ((size_t)j * g.S + kb) * D * 2;
-      const char* vblk = vg + (size_t)j * g.S * D * 2 + kb * 2;
+      const uint32_t ko = (uint32_t)(((size_t)j * g.S + kb) * D * 2);
+      const uint32_t vo = (uint32_t)((size_t)j * g.S * D * 2 + kb * 2);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous block's LDS reads are done
 #pragma unroll
       for (int q = 0; q < NKI; ++q) {
         const int e = 64 * q + lane;
         const int row = e / KPR, col = e % KPR;
-        __builtin_amdgcn_global_load_lds((const void*)(kblk + row * D * 2 + (col == KPR - 1 ? 0 : col * 16)),
-                                         (lds_void*)((char*)mk + 1024 * q), 16, 0, 0);
+        buffer_load_lds16(kg, head_bytes, (char*)mk + 1024 * q, row * D * 2 + (col == KPR - 1 ? 0 : col * 16), ko);
       }
 #pragma unroll
       for (int q = 0; q < NVI; ++q) {
         const int e = 64 * q + lane;
         const int row = e / VPR, col = e % VPR;
-        __builtin_amdgcn_global_load_lds((const void*)(vblk + (size_t)row * g.S * 2 + (col == VPR - 1 ? 0 : col * 16)),
-                                         (lds_void*)((char*)mv + 1024 * q), 16, 0, 0);
+        buffer_load_lds16(vg, head_bytes, (char*)mv + 1024 * q, row * g.S * 2 + (col == VPR - 1 ? 0 : col * 16), vo);
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the block is in LDS
       // S^T = K Q^T; keys of st[h2][i]: 32*h2 + 8*(i/4) + 4*lh + (i%4)
@@ -216,6 +214,8 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
 }
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s) {
+  // buffer descriptors address one KV head's rows with 32-bit offsets
+  if ((size_t)a.g.NS * a.g.D * 2 > 0x7fffffffu) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.g.Hkv * a.decode_chunks));
   if (a.g.D == 128)
     hipLaunchKernelGGL((k_attn_decode<128>), grid, dim3(64 * DW), 0, s, a);

@@ -117,6 +117,10 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding (n < 64; exp and lgkm counters not waited on)
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // 16 bytes per lane from base + voff + soff (a buffer of `bytes` bytes; reads
 // past it return 0) into LDS at lds + 16 * lane (lds wave-uniform).  A buffer
 // load (MUBUF) rather than global_load_lds: the compiler counts a pending FLAT

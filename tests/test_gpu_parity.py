@@ -141,6 +141,15 @@ def test_full_config_sampled(name):
     _case(workloads.get(name), rows="sample", tokens_per_cube=2, extra_tokens=8)
 
 
+def test_decode_mode_four_cubes_one_chunk():
+    # a decode over a cache of 4 cubes runs the decode kernel as a single
+    # chunk: its partial rows still need (and now get) workspace
+    wl = workloads.Workload(name="decode_4cubes", T=4, H=8, W=8, ct=4, ch=4, cw=4, n_q_heads=4,
+                            n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7, seed=39,
+                            video_queries=False, n_decode=2)
+    _case(wl)
+
+
 def test_decode_single_step():
     """One decode step (1 query token x 28 heads) over the full decode cache."""
     wl = workloads.get("decode").replace(n_decode=1, name="decode_step")
