@@ -44,13 +44,20 @@ def _bf16_normal(rng, shape):
     return workloads.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
 
 
-def _lists(layer, wl, g):
-    """Device selection of every row: ({(hq, pos): cubes}, {(hq, m): cubes})."""
+def _lists(layer, wl, g, video_rows=None):
+    """Device selection of every row (or of the video rows listed):
+    ({(hq, pos): cubes}, {(hq, m): cubes})."""
     cnt = layer.sel_count.cpu().numpy()
     idx = layer.sel_idx.cpu().numpy()
     capv = g.S * g.n_cubes * (g.n_cubes - 1) // 2 if wl.video_queries else 0
     n_extra = wl.n_decode
     sv, sx = {}, {}
+    if video_rows is not None:
+        for hq, p in video_rows:
+            c, r = divmod(p, g.S)
+            o = hq * capv + g.S * c * (c - 1) // 2 + r * c
+            sv[(hq, p)] = idx[o:o + cnt[hq, p]].tolist()
+        return sv, sx
     for hq in range(wl.n_q_heads):
         if wl.video_queries:
             for p in range(g.N):
@@ -69,7 +76,13 @@ def _err(got, ref):
     return np.abs(got - ref) / np.maximum(rms, 1e-30)
 
 
-def _run_case(wl, p=None, seed=0):
+def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
+    """Forward with log-sum-exp and backward on the device, graded against the
+    float64 oracle over the device's selection.  video_rows: only these
+    (hq, pos) rows are differentiated by the oracle (all rows by default);
+    key_cubes: dK and dV are compared on the keys of these cubes only, which
+    must be attended by listed rows alone (e.g. the last cubes when every row
+    of them is listed)."""
     from adaptive_cube_sparse_amd import AdasAttentionGrad
     p = wl.p if p is None else p
     log(f"[bwd] {wl.name} grid {wl.T}x{wl.H}x{wl.W} cube ({wl.ct},{wl.ch},{wl.cw}) heads {wl.n_q_heads}/"
@@ -88,7 +101,7 @@ def _run_case(wl, p=None, seed=0):
     dq, dqx, dk, dv = layer.backward(to_dev(dout, dev) if dout is not None else None,
                                      to_dev(doutx, dev) if doutx is not None else None, qx)
     torch.cuda.synchronize()
-    sv, sx = _lists(layer.fwd, wl, g)
+    sv, sx = _lists(layer.fwd, wl, g, video_rows)
     q_cube = O.partition(data["q"], g)[0] if wl.video_queries else np.zeros((wl.n_q_heads, g.N, wl.head_dim), np.uint16)
     k_cube, _ = O.partition(data["k"], g)
     v_cube, _ = O.partition(data["v"], g)
@@ -133,8 +146,11 @@ def _run_case(wl, p=None, seed=0):
     log(f"  dq: largest error / bound {worst:.3f} over {len(rows)} rows")
     assert worst <= 1.0
     errs = {}
-    errs["dk"] = _err(dk.cpu().numpy(), ref["dk_raster"])
-    errs["dv"] = _err(dv.cpu().numpy(), ref["dv_raster"])
+    keys = slice(None)
+    if key_cubes is not None:
+        keys = np.sort(np.concatenate([perm[j * g.S:(j + 1) * g.S] for j in key_cubes]))
+    errs["dk"] = _err(dk.cpu().numpy()[keys], ref["dk_raster"][keys])
+    errs["dv"] = _err(dv.cpu().numpy()[keys], ref["dv_raster"][keys])
     log("  lse max-abs %.2e; " % lerr + ", ".join(f"{k}: max {e.max():.2e} mean {e.mean():.2e}" for k, e in errs.items()))
     assert lerr <= 1e-3
     for k, e in errs.items():
@@ -172,3 +188,19 @@ def test_bwd_many_cubes_and_tiles():
     # 64 cubes, 7 query heads per KV head: tiles of 256 rows span head slots,
     # early cubes are attended by hundreds of rows
     _run_case(_small(name="bwd_mid", T=16, H=16, W=16, n_q_heads=7, n_kv_heads=1, seed=4105), p=0.7)
+
+
+def test_bwd_qwen3b_full_size_sampled():
+    # the 3B-shaped layer bench.py --backward times (16/2 heads, 256 cubes of
+    # 64, p = 0.7): every row of the last two cubes (so dK and dV of their keys
+    # are complete sums) plus 2 rows per head in cubes spread over the layer
+    wl = workloads.get("qwen3b")
+    g = O.Geometry.of(wl)
+    Nc, S = g.n_cubes, g.S
+    rng = np.random.default_rng(4106)
+    rows = {(hq, p) for hq in range(wl.n_q_heads) for p in range((Nc - 2) * S, Nc * S)}
+    for c in (0, 1, Nc // 4, Nc // 2, 3 * Nc // 4, Nc - 3):
+        for hq in range(wl.n_q_heads):
+            for r in rng.choice(S, size=2, replace=False):
+                rows.add((hq, c * S + int(r)))
+    _run_case(wl, video_rows=sorted(rows), key_cubes=[Nc - 2, Nc - 1])
