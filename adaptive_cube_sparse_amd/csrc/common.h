@@ -247,24 +247,35 @@ __device__ int topp_select_row(const float (&E)[NPL], int n, float Z, float p,
       }
     }
   }
-  // mass strictly above tau and the number of ties at tau
-  float mgt = 0.0f;
+  // ties at tau; with at most one (the usual case) the set is {E >= tau}.
+  // Otherwise the mass strictly above tau fixes how many of them to take.
   int ceq = 0;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    mgt += E[i] > tau ? E[i] : 0.0f;
-    ceq += popc64(__ballot(E[i] == tau));
-  }
-  mgt = wave_sum(mgt);
+  for (int i = 0; i < NPL; ++i) ceq += popc64(__ballot(E[i] == tau));
   int keq = ceq;
-  if (tau > 0.0f) {
+  if (ceq > 1) {
+    float mgt = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) mgt += E[i] > tau ? E[i] : 0.0f;
+    mgt = wave_sum(mgt);
     const float need = (target - mgt) / tau;
     int k = (int)ceilf(need);
     if (k < 1) k = 1;
     if (k < keq) keq = k;
   }
   // ascending compaction: stripe i holds candidates 64*i .. 64*i+63
-  int base = 0, eq_seen = 0;
+  int base = 0;
+  if (keq == ceq) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const bool sel = E[i] >= tau;
+      const uint64_t bs = __ballot(sel);
+      if (sel) out[base + lanes_below(bs)] = lane + kWave * i;
+      base += popc64(bs);
+    }
+    return base;
+  }
+  int eq_seen = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const bool eq = E[i] == tau;

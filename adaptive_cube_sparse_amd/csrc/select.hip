@@ -98,7 +98,6 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& 
   }
 }
 
-constexpr int kSelWaves = 8;
 
 // The split path serves extra rows with more than 1024 candidates when a KV
 // head has few of them (at most 64, e.g. decode steps); many extra rows fill
@@ -108,9 +107,11 @@ bool use_split_select(const KGeom& g, int n_extra, int gmax) {
 }
 
 // RT rows per tile (a multiple of 16, or 8), NPL candidate slots per lane
-// (capacity 64 * NPL).  Eight waves share every kbar load across RT rows.
-template <int D, int RT, int NPL>
-__global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, TileSched ts) {
+// (capacity 64 * NPL), NW waves that share every kbar load across RT rows.
+// Bands whose logits fill most of the LDS (one workgroup per CU) take 16
+// waves, so that each SIMD still holds four of them.
+template <int D, int RT, int NPL, int NW>
+__global__ __launch_bounds__(64 * NW) void k_select_bf16(SelectArgs a, TileSched ts) {
   constexpr int NCAP = kWave * NPL;
   constexpr int RB = (RT + 15) / 16;  // 16-row MFMA blocks
   __shared__ float sZ[RT * NCAP];
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
   const float scale = 1.0f / sqrtf((float)D);
   const float* kb = a.kbar + (size_t)grp * (g.NS / g.S) * D;
   const int nblk = (n + 15) / 16;
-  for (int blk = wave; blk < nblk; blk += kSelWaves) {
+  for (int blk = wave; blk < nblk; blk += NW) {
     const int j = blk * 16 + lane % 16;
     const int jj = j < n ? j : n - 1;
     f32x4 acc[RB];
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_bf16(SelectArgs a, Ti
   // ---- phase B: softmax + Top-p, one row at a time per wave ------------------
   // The row's LDS logits are dead once loaded, so they serve as the wave's
   // 64-float scratch for the Top-p gather.
-  for (int row = wave; row < RT; row += kSelWaves) {
+  for (int row = wave; row < RT; row += NW) {
     const int rho = rho0 + row;
     if (rho >= group_rows) break;
     const RowRef rr = video ? video_row(a.hg, grp, n, g.S, rho) : extra_row(a.hg, grp, a.n_extra, rho);
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_vide
 
 // One launch serves video query cubes [c_lo, c_hi) and, if with_extra, the
 // extra rows (which have Nc candidates).
-template <int D, int RT, int NPL>
+template <int D, int RT, int NPL, int NW>
 static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, bool with_extra) {
   TileSched ts;
   const int gmax = a.hg.gmax;
@@ -639,7 +640,7 @@ static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, 
   const int nc = a.has_video && c_hi > c_lo ? c_hi - c_lo : 0;
   const int blocks = ts.n_extra_tiles + nc * a.g.Hkv * ts.video_tiles_per_group;
   if (blocks > 0)
-    hipLaunchKernelGGL((k_select_bf16<D, RT, NPL>), dim3(blocks), dim3(64 * kSelWaves), 0, s, a, ts);
+    hipLaunchKernelGGL((k_select_bf16<D, RT, NPL, NW>), dim3(blocks), dim3(64 * NW), 0, s, a, ts);
 }
 
 // Video rows of query cube c have c candidates; split them by capacity so
@@ -656,15 +657,15 @@ static void launch_bf16_all(const SelectArgs& a, hipStream_t s) {
     const bool ex = extra && Nc > lo && Nc <= hi;
     if (h > l || ex) launch(l, h, ex);
   };
-  band([&](int l, int h, bool ex) { launch_bf16<D, 8, 64>(a, s, l, h, ex); }, 2048, 4096);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 16, 32>(a, s, l, h, ex); }, 1024, 2048);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 16>(a, s, l, h, ex); }, 768, 1024);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 12>(a, s, l, h, ex); }, 512, 768);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 8>(a, s, l, h, ex); }, 384, 512);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 6>(a, s, l, h, ex); }, 256, 384);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 4>(a, s, l, h, ex); }, 128, 256);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 2>(a, s, l, h, ex); }, 64, 128);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 1>(a, s, l, h, ex); }, 0, 64);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 8, 64, 16>(a, s, l, h, ex); }, 2048, 4096);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 16, 32, 16>(a, s, l, h, ex); }, 1024, 2048);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 16, 16>(a, s, l, h, ex); }, 768, 1024);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 12, 16>(a, s, l, h, ex); }, 512, 768);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 8, 8>(a, s, l, h, ex); }, 384, 512);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 6, 8>(a, s, l, h, ex); }, 256, 384);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 4, 8>(a, s, l, h, ex); }, 128, 256);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 2, 8>(a, s, l, h, ex); }, 64, 128);
+  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 1, 8>(a, s, l, h, ex); }, 0, 64);
   if (split) {
     // split path for the extra rows (workspace holds their logits)
     hipLaunchKernelGGL((k_select_scores<D>), dim3((Nc + 63) / 64, a.g.Hkv), dim3(256), 0, s, a);
