@@ -213,6 +213,7 @@ void plan_attention(AttnArgs& a, adas_dtype dt) {
     const int want = (256 + a.g.Hkv - 1) / a.g.Hkv;
     int cubes = (a.g.Nc + want - 1) / want;
     cubes = ((cubes + decode_waves() - 1) / decode_waves()) * decode_waves();
+    if (cubes > decode_max_chunk_cubes()) cubes = decode_max_chunk_cubes();
     a.extra_chunk_cubes = cubes;
     a.decode_chunks = (a.g.Nc + cubes - 1) / cubes;
     a.extra_tiles_per_group = 1;

@@ -25,9 +25,11 @@ typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kLazyD = 8.0f;  // rescale only when a block max exceeds the reference by 2^8
 constexpr int DW = 4;           // waves per workgroup
+constexpr int DMAXL = 128;      // cubes per wave and chunk (list capacity)
 }  // namespace
 
 int decode_waves() { return DW; }
+int decode_max_chunk_cubes() { return DW * DMAXL; }
 
 // Requires S % 64 == 0 and at most 32 rows per KV head (host checks).
 template <int D>
@@ -85,30 +87,66 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
   void* const vg = (void*)((const uint16_t*)a.v_cube + (size_t)grp * g.NS * D);  // [Nc][D][S]
   const int c0 = chunk * a.extra_chunk_cubes;
   const int c1 = min(g.Nc, c0 + a.extra_chunk_cubes);
+  // This wave's cubes (c0 + wave, + DW, ...) that some row selected, with the
+  // rows that selected them, listed in LDS private to the wave.
+  __shared__ uint32_t s_cube[DW][DMAXL], s_rmask[DW][DMAXL];
+  int n_list = 0;
   for (int j = c0 + wv; j < c1; j += DW) {
     const uint32_t bit = (row_ok && lh == 0) ? (rbits[j >> 5] >> (j & 31)) & 1u : 0u;
     const uint32_t mask = (uint32_t)__ballot(bit != 0u);  // rows of the wave that selected j
-    if (mask == 0u) continue;
-    const bool rowsel = ((mask >> lr) & 1u) != 0u;
-    for (int kb = 0; kb < g.S; kb += 64) {
-      // piece e = 64*q + lane of the padded block; the padding column re-reads
-      // the row's first piece
-      const uint32_t ko = (uint32_t)(((size_t)j * g.S + kb) * D * 2);
-      const uint32_t vo = (uint32_t)((size_t)j * g.S * D * 2 + kb * 2);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous block's LDS reads are done
-#pragma unroll
-      for (int q = 0; q < NKI; ++q) {
-        const int e = 64 * q + lane;
-        const int row = e / KPR, col = e % KPR;
-        buffer_load_lds16(kg, head_bytes, (char*)mk + 1024 * q, row * D * 2 + (col == KPR - 1 ? 0 : col * 16), ko);
+    if (mask != 0u) {
+      if (lane == 0) {
+        s_cube[wv][n_list] = (uint32_t)j;
+        s_rmask[wv][n_list] = mask;
       }
+      ++n_list;
+    }
+  }
+  // Key blocks b = (list entry b / nkbc, block b % nkbc of its cube).  K and
+  // V^T of block b + 1 are loaded while block b computes: K(b+1) as soon as the
+  // score MFMAs have read K(b), V^T(b+1) once the output MFMAs have read
+  // V^T(b).  Loads into LDS return in order, so "at most NVI loads pending"
+  // after K(b), V(b) were issued means K(b) has landed, and "at most NKI
+  // pending" after K(b+1) was issued means V(b) has landed.
+  const int nkbc = g.S / 64;
+  const int nb = n_list * nkbc;
+  auto block_offsets = [&](int b, uint32_t& ko, uint32_t& vo) __attribute__((always_inline)) {
+    const int e = b / nkbc, kb = (b - e * nkbc) * 64;
+    const int j = __builtin_amdgcn_readfirstlane((int)s_cube[wv][e]);  // wave-uniform: scalar offsets
+    ko = (uint32_t)(((size_t)j * g.S + kb) * D * 2);
+    vo = (uint32_t)((size_t)j * g.S * D * 2 + kb * 2);
+  };
+  // piece e = 64*q + lane of the padded block; the padding column re-reads
+  // the row's first piece
+  auto issue_k = [&](uint32_t ko) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < NVI; ++q) {
-        const int e = 64 * q + lane;
-        const int row = e / VPR, col = e % VPR;
-        buffer_load_lds16(vg, head_bytes, (char*)mv + 1024 * q, row * g.S * 2 + (col == VPR - 1 ? 0 : col * 16), vo);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the block is in LDS
+    for (int q = 0; q < NKI; ++q) {
+      const int e = 64 * q + lane;
+      const int row = e / KPR, col = e % KPR;
+      buffer_load_lds16(kg, head_bytes, (char*)mk + 1024 * q, row * D * 2 + (col == KPR - 1 ? 0 : col * 16), ko);
+    }
+  };
+  auto issue_v = [&](uint32_t vo) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NVI; ++q) {
+      const int e = 64 * q + lane;
+      const int row = e / VPR, col = e % VPR;
+      buffer_load_lds16(vg, head_bytes, (char*)mv + 1024 * q, row * g.S * 2 + (col == VPR - 1 ? 0 : col * 16), vo);
+    }
+  };
+  if (nb > 0) {
+    uint32_t ko, vo;
+    block_offsets(0, ko, vo);
+    issue_k(ko);
+    issue_v(vo);
+  }
+  for (int b = 0; b < nb; ++b) {
+    const bool rowsel = ((s_rmask[wv][b / nkbc] >> lr) & 1u) != 0u;
+    const bool has_next = b + 1 < nb;
+    uint32_t kon = 0, von = 0;
+    if (has_next) block_offsets(b + 1, kon, von);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NVI));  // K(b) is in LDS
+    {
       // S^T = K Q^T; keys of st[h2][i]: 32*h2 + 8*(i/4) + 4*lh + (i%4)
       df32x16 st[2];
 #pragma unroll
@@ -122,6 +160,8 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
           st[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ds], st[h2], 0, 0, 0);
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the K fragments are read
+      if (has_next) issue_k(kon);
       // online softmax in log2 units with lazy rescaling
       float mb = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
@@ -155,6 +195,8 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
         }
       ls += xor32_f32(ls);
       l_run += ls;
+      if (has_next) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NKI));  // V^T(b) is in LDS
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       // O^T += V^T P^T; slot 8*lh + e of k-step u holds key 16*u + 8*(e/4) + 4*lh + (e%4),
       // kept by ADAS_LAYOUT_VT in column 16*u + 8*lh + e
 #pragma unroll
@@ -165,12 +207,15 @@ __global__ __launch_bounds__(64 * DW, 1) void k_attn_decode(AttnArgs a) {
               dbf16x8, *reinterpret_cast<const uint4*>(&mv[(32 * db + lr) * VS + 16 * u + 8 * lh]));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], acc[db], 0, 0, 0);
         }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the V^T fragments are read
+      if (has_next) issue_v(von);
     }
   }
   // The four waves' states are merged in LDS (the block buffers are free now)
   // into one partial row per (KV head, chunk): [grp][chunk][32 rows][D + 2].
   constexpr int RS = D + 2;
   static_assert(DW * 32 * RS * 4 <= DW * (64 * KS + D * VS) * 2, "merge area fits the block buffers");
+  static_assert(NKI < 64 && NVI < 64, "vmcnt range");
   float* red = reinterpret_cast<float*>(&lds_k[0][0]);  // [wave][row][RS], spans lds_k then lds_v
   __syncthreads();  // every wave is done with its block buffer
   if (row_ok) {

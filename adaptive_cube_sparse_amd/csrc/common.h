@@ -417,5 +417,6 @@ hipError_t launch_union(const AttnArgs& a, hipStream_t s);
 int union_tile_rows();  // rows per tile of the union kernel
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s);
 int decode_waves();     // waves per workgroup of the decode kernel
+int decode_max_chunk_cubes();  // most cubes in one chunk of the decode kernel
 
 }  // namespace adas
