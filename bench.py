@@ -209,6 +209,42 @@ def decode_unique_bytes(layer, wl) -> int:
     return kv_bytes + qo + list_entries * 4 + Hq * n_extra * 4
 
 
+def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict) -> dict:
+    """Each step of the path against the MI355X peak that bounds it: the
+    cube gather (partition of Q, K, V: every element read and written once,
+    plus perm) and the mean-key reduction (K read, float32 mean keys written)
+    against HBM; the selection's scoring product (2 d flops per candidate of
+    every row) against the bf16 MFMA peak; the attention call as in the
+    roofline.  For decode workloads the gather and reduction are those of the
+    cache build, timed once before the steps."""
+    el = 2 if wl.dtype == "bf16" else 4
+    d, N, Hq, Hkv = wl.head_dim, wl.n_tokens, wl.n_q_heads, wl.n_kv_heads
+    S = wl.cube_size
+    Nc = N // S
+    q_el = N * Hq * d if wl.video_queries else 0
+    kv_el = N * Hkv * d
+    out = {}
+    if "gather" in st_ms:
+        b = 2 * el * (q_el + 2 * kv_el) + 4 * N
+        out["gather"] = {"ms": st_ms["gather"], "bytes": b, "bound": "hbm",
+                         "GB/s": b / (st_ms["gather"] * 1e-3) / 1e9,
+                         "frac": b / (st_ms["gather"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if "mean_keys" in st_ms:
+        b = el * kv_el + 4 * Hkv * Nc * d
+        out["mean_keys"] = {"ms": st_ms["mean_keys"], "bytes": b, "bound": "hbm",
+                            "GB/s": b / (st_ms["mean_keys"] * 1e-3) / 1e9,
+                            "frac": b / (st_ms["mean_keys"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    cand = (Hq * S * Nc * (Nc - 1) // 2 if wl.video_queries else 0) + Hq * n_extra * Nc
+    f = 2.0 * d * cand
+    t = f / (st_ms["select"] * 1e-3) / 1e12
+    out["select"] = {"ms": st_ms["select"], "scoring_flops": f, "scoring_TFLOP/s": t,
+                     "scoring_frac_of_bf16_peak": t / PEAK_BF16_TFLOPS,
+                     "bound": "alu (Top-p search; the scoring product is a small share)"}
+    out["attention"] = {"ms": roof["launch_ms"], "bound": roof["bound"], "achieved": roof["achieved"],
+                        "unit": roof["unit"], "frac": roof["frac"]}
+    return out
+
+
 def cpu_baseline(wl, data, budget_s: float, topk: int = 0):
     """Time the CPU oracle on a bounded, seeded sample of the workload's rows:
     selection softmax + Top-p + attention per row (partition and mean keys of
@@ -516,29 +552,54 @@ def main():
     kt = up(data["k_text"]) if n_text_kv else None
     vt = up(data["v_text"]) if n_text_kv else None
     stream = torch.cuda.current_stream()
-    if decode:
-        layer.build_kv(k, v)   # the cache exists before decoding starts
+    from adaptive_cube_sparse_amd import ADAS_LAYOUT_VT, adas_cube_mean_keys, adas_cube_partition
 
-    ev = {name: [] for name in ("layout", "select", "attention")}
+    def mark():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def layout(record):
+        """Partition K, V (and Q), then the mean keys: the calls of
+        AdasAttention.build_kv / partition_queries, with an event between the
+        gather and the reduction."""
+        g = layer.geom
+        e0 = mark() if record else None
+        adas_cube_partition(g, k, layer.k_cube, layer.perm)
+        adas_cube_partition(g, v, layer.v_cube, None, layout=ADAS_LAYOUT_VT)
+        if q is not None:
+            adas_cube_partition(g, q, layer.q_cube, None)
+        e1 = mark() if record else None
+        adas_cube_mean_keys(g, layer.k_cube, layer.kbar)
+        e2 = mark() if record else None
+        return e0, e1, e2
+
+    ev = {name: [] for name in ("layout", "gather", "mean_keys", "select", "attention")}
+    if decode:
+        # the cache exists before decoding starts; its build is timed once here
+        for _ in range(2):
+            lay = layout(True)
+        torch.cuda.synchronize()
+        ev["gather"].append((lay[0], lay[1]))
+        ev["mean_keys"].append((lay[1], lay[2]))
 
     def step(record):
-        def mark():
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(stream)
-            return e
-        e0 = mark() if record else None
+        e0 = e1 = None
         if not decode:
-            layer.build_kv(k, v)
-            layer.partition_queries(q)
-        e1 = mark() if record else None
+            e0, e1, e2 = layout(record)
+        else:
+            e2 = mark() if record else None
         layer.select(qe)
-        e2 = mark() if record else None
-        layer.attend(qe, kt, vt)
         e3 = mark() if record else None
+        layer.attend(qe, kt, vt)
+        e4 = mark() if record else None
         if record:
-            ev["layout"].append((e0, e1))  # partition Q/K/V + mean keys
-            ev["select"].append((e1, e2))
-            ev["attention"].append((e2, e3))
+            if not decode:
+                ev["layout"].append((e0, e2))  # partition Q/K/V + mean keys
+                ev["gather"].append((e0, e1))
+                ev["mean_keys"].append((e1, e2))
+            ev["select"].append((e2, e3))
+            ev["attention"].append((e3, e4))
 
     for _ in range(args.warmup):
         step(False)
@@ -553,7 +614,8 @@ def main():
     def mean_ms(pairs):
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
 
-    k_ms = {name: mean_ms(p) for name, p in ev.items() if p}
+    k_ms = {name: mean_ms(p) for name, p in ev.items() if p and name in ("layout", "select", "attention")}
+    st_ms = {name: mean_ms(p) for name, p in ev.items() if p}
     pairs = attended_pairs(layer, wl)
     flops_step = 4.0 * wl.head_dim * pairs
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -572,6 +634,7 @@ def main():
                 "algorithmic_flops_per_launch": flops_step}
     roof["kernels"] = attention_kernels(wl, n_extra)
     roof["launch_ms"] = attn_ms  # one adas_sparse_attn_fwd call: the kernels above
+    stages = stage_rates(wl, n_extra, st_ms, roof)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -595,6 +658,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_ms": k_ms,
+        "stages": stages,
         "queries_per_s": rows / (ms_step * 1e-3),
         "attended_pairs": pairs,
         "mean_selected_fraction": dens,
