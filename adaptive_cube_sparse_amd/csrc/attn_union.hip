@@ -3,11 +3,14 @@
 // full attention to the own cube; one exact softmax, scale 1/sqrt(d_k)).
 // bf16 MFMA kernel with union tiles.
 //
-// A workgroup (8 waves) owns a tile of 256 rows that read the same KV head
-// (video rows of one query cube, or extra rows).  Each wave owns 32 rows; their
-// query operands and float32 output accumulators stay in registers for the
-// whole tile.  The workgroup walks the union of its rows' selected cubes (plus
-// the own cube, or the causal text keys), one key block of 64 keys at a time:
+// A workgroup (8 waves) owns a tile of 256 rows that read the same KV head:
+// consecutive video rows, numbered query cube by query cube from the last (a
+// tile may span two or more query cubes), or extra rows.  Each wave owns 32
+// rows; their query operands and float32 output accumulators stay in
+// registers for the whole tile.  The workgroup walks the union of the cubes
+// its rows attend (selected cubes and, for video rows, their own cubes, in
+// descending order; for text rows also the causal text keys), one key block of
+// 64 keys at a time:
 //   * K rows and V^T rows (values arrive cube-transposed, ADAS_LAYOUT_VT) of a
 //     block are staged in LDS.  When every block is full (S a multiple of 64)
 //     video blocks move global -> LDS with buffer_load_dwordx4 ... lds over
@@ -15,20 +18,19 @@
 //     otherwise, and for text keys, through registers one block ahead with
 //     one barrier per block;
 //   * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, applies a
-//     per-row selection bit (row x cube bitmap built from the selection lists)
-//     as a +inf softmax bias, keeps the online softmax in log2 units with lazy
-//     rescaling, and accumulates O^T += V^T P^T.  On full blocks the softmax
-//     unit is half a block (32 keys) and the units are software-pipelined:
-//     the exp / convert instructions of one unit are issued between the
-//     MFMAs of its neighbours.  A wave none of whose rows selected a pair of
-//     blocks skips the pair.
+//     per-row bit (row x cube bitmap built from the selection lists and the
+//     rows' own cubes) as a +inf softmax bias, keeps the online softmax in log2
+//     units with lazy rescaling, and accumulates O^T += V^T P^T.  On full
+//     blocks the softmax unit is half a block (32 keys) and the units are
+//     software-pipelined: the exp / convert instructions of one unit are
+//     issued between the MFMAs of its neighbours.
 // Rows spend MFMA work on every key block of the tile union; the masked part is
 // the price of keeping accumulators in registers.
 //
-// Tile order: extra rows first (heaviest), then video tiles by descending
-// query cube.  When 8 is a multiple of the KV head count, workgroup b runs on
-// XCD b % 8 (round-robin dispatch) and video tiles are dealt so that each XCD
-// serves one KV head, letting concurrently resident tiles share K/V in L2.
+// Tile order: extra rows first (heaviest), then video tiles from the last
+// query cube down.  When 8 is a multiple of the KV head count, workgroup b runs
+// on XCD b % 8 (round-robin dispatch) and video tiles are dealt so that each
+// XCD serves one KV head, letting concurrently resident tiles share K/V in L2.
 #include <type_traits>
 
 #include "common.h"
@@ -64,7 +66,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 int union_tile_rows() { return UTR; }
 
 struct USched {
-  int video_tiles_per_group;
+  int video_tiles_per_group;  // video tiles per KV head (its rows over every query cube)
   int extra_tiles_per_group;
   int extra_chunks;
   int extra_chunk_cubes;
@@ -125,31 +127,29 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     grp = tile_e / sc.extra_tiles_per_group;
     rho0 = (tile_e - grp * sc.extra_tiles_per_group) * UTR;
   } else {
+    // video tile t of KV head grp: rows rho0 .. rho0 + UTR of the head's video
+    // rows, numbered query cube by query cube from the last (head slot, offset
+    // inside a cube), so a tile may span two or more query cubes
     video = true;
     b -= sc.n_extra_wgs;
-    const int tpg = sc.video_tiles_per_group;
+    int t;
     if (sc.xcd_mode) {
       const int x = b & 7, i = b >> 3;
-      const int stride_c = 8 / g.Hkv;
       grp = x % g.Hkv;
-      const int cpar = x / g.Hkv;
-      const int ci = i / tpg;
-      rho0 = (i - ci * tpg) * UTR;
-      c = g.Nc - 1 - cpar - ci * stride_c;
-      if (c < 0) return;
+      t = x / g.Hkv + i * (8 / g.Hkv);
     } else {
-      const int per_c = g.Hkv * tpg;
-      c = g.Nc - 1 - b / per_c;
-      const int rem = b % per_c;
-      grp = rem / tpg;
-      rho0 = (rem - grp * tpg) * UTR;
+      grp = b % g.Hkv;
+      t = b / g.Hkv;
     }
+    if (t >= sc.video_tiles_per_group) return;
+    rho0 = t * UTR;
   }
   const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
-  const int group_rows = video ? gsz * g.S : gsz * a.n_extra;
+  const int group_rows = video ? gsz * g.N : gsz * a.n_extra;
   const int n_rows = min(UTR, group_rows - rho0);
   if (n_rows <= 0) return;
   const int hstart = a.hg.start[grp];
+  if (video) c = g.Nc - 1 - rho0 / (gsz * g.S);  // the tile's highest query cube
 
   // ---- this lane's row ------------------------------------------------------------
   const int t_row = wave * 32 + lr;
@@ -158,9 +158,11 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   if (row_ok) {
     const int rho = rho0 + t_row;
     if (video) {
-      const int slot = rho / g.S;
+      const int ci = rho / (gsz * g.S);
+      const int rem = rho - ci * gsz * g.S;
+      const int slot = rem / g.S;
       hq = a.hg.heads[hstart + slot];
-      pos = c * g.S + (rho - slot * g.S);
+      pos = (g.Nc - 1 - ci) * g.S + (rem - slot * g.S);
     } else {
       const int slot = rho / a.n_extra;
       hq = a.hg.heads[hstart + slot];
@@ -645,38 +647,6 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     }
   }
 
-  // ---- own cube (video): every row ------------------------------------------------------
-  if (video) {
-    if constexpr (FULL) {
-      dpipeline(
-          nkb_cube,
-          [&](int i, uint32_t& ko, uint32_t& vo) __attribute__((always_inline)) {
-            ko = (uint32_t)(((size_t)c * g.S + i * UKB) * D * 2);
-            vo = (uint32_t)((size_t)c * g.S * D * 2 + i * UKB * 2);
-          },
-          [&](int, const uint16_t* kb0, const uint16_t* vb0, const uint16_t* kb1, const uint16_t* vb1,
-              bool two) __attribute__((always_inline)) {
-            if (!wave_has_rows) return;
-            if (two) block2(kb0, vb0, row_ok, kb1, vb1, row_ok);
-            else block1(kb0, vb0, row_ok);
-          });
-    } else {
-    pipeline(
-        true, nkb_cube,
-        [&](int i, const uint16_t*& kp_, const uint16_t*& vp_, size_t& st_, int& kc_) __attribute__((always_inline)) {
-          const size_t off = ((size_t)c * g.S + i * UKB) * D;
-          kp_ = kg + off;
-          vp_ = vg + (size_t)c * g.S * D + i * UKB;
-          st_ = D;
-          kc_ = min(UKB, g.S - i * UKB);
-        },
-        [&](int, int buf, int kc) __attribute__((always_inline)) {
-          if (!wave_has_rows) return;
-          if (FULL || kc == UKB) compute(kFull{}, kbuf_rt(buf), vbuf_rt(buf), row_ok, kc, false, 0);
-          else compute(kMasked{}, kbuf_rt(buf), vbuf_rt(buf), row_ok, kc, false, 0);
-        });
-    }
-  }
   // ---- causal text keys (extra rows of a text prefill), chunk 0 --------------------------
   if (!video && a.n_text_kv > 0 && chunk == 0) {
     const uint16_t* kt = (const uint16_t*)a.k_text + (size_t)grp * D;
@@ -695,28 +665,37 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         });
   }
 
-  // ---- selected cubes -----------------------------------------------------------------
-  // video rows: two threads per row walk the row's ascending list
+  // ---- selected cubes (video rows: and their own cubes) ---------------------------------
+  // video rows: two threads per row walk the row's ascending list; the row's
+  // own cube is one more bit of the same bitmap
   const int my_row = tid >> 1, my_half = tid & 1;
   const int32_t* my_list = nullptr;
-  int my_cnt = 0;
+  int my_cnt = 0, my_c = -1;
   if (video && my_row < n_rows) {
     const int rho = rho0 + my_row;
-    const int slot = rho / g.S;
+    const int ci = rho / (gsz * g.S);
+    const int rem = rho - ci * gsz * g.S;
+    const int slot = rem / g.S;
     const int hq2 = a.hg.heads[hstart + slot];
-    const int r = rho - slot * g.S;
-    my_list = a.sel_idx + video_list_offset(a.capv, hq2, g.S, c, r);
-    my_cnt = a.sel_count[(size_t)hq2 * a.rows_per_head + c * g.S + r];
+    const int r = rem - slot * g.S;
+    my_c = g.Nc - 1 - ci;
+    my_list = a.sel_idx + video_list_offset(a.capv, hq2, g.S, my_c, r);
+    my_cnt = a.sel_count[(size_t)hq2 * a.rows_per_head + my_c * g.S + r];
   }
   int cube_lo, cube_hi;
   if (video) {
     cube_lo = 0;
-    cube_hi = c;
+    cube_hi = c + 1;
   } else {
     cube_lo = chunk * sc.extra_chunk_cubes;
     cube_hi = min(g.Nc, cube_lo + sc.extra_chunk_cubes);
   }
-  for (int jb = cube_lo; jb < cube_hi; jb += UPASS) {
+  // Passes and the cubes inside a pass run in descending order, so a video
+  // row meets its own cube (the highest it attends) first and takes its
+  // softmax reference there.
+  const int n_pass = (cube_hi - cube_lo + UPASS - 1) / UPASS;
+  for (int ps = n_pass - 1; ps >= 0; --ps) {
+    const int jb = cube_lo + ps * UPASS;
     const int je = min(cube_hi, jb + UPASS);
     const int span = je - jb;
     __syncthreads();  // previous users of bits/ulist are done
@@ -747,14 +726,15 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       uint32_t* wbase = &s_bits[my_row >> 5];
 #pragma unroll 4
       for (int i = lo + my_half; i < lo2; i += 2) atomicOr(wbase + UNW * (my_list[i] - jb), bit);
+      if (my_half == 0 && my_c >= jb && my_c < je) atomicOr(wbase + UNW * (my_c - jb), bit);
     }
     __syncthreads();
     if (wave == 0) {
       int base = 0;
       for (int u0 = 0; u0 < span; u0 += 64) {
-        const int u = u0 + lane;
+        const int u = span - 1 - (u0 + lane);  // descending
         bool any = false;
-        if (u < span) {
+        if (u >= 0) {
           uint32_t o = 0;
 #pragma unroll
           for (int w = 0; w < UNW; ++w) o |= s_bits[UNW * u + w];
@@ -784,7 +764,9 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
             // rows all pass over a block is rare): one code path keeps the
             // accumulators in place instead of copying them where paths meet.
             // An odd last block pairs with the other buffer's stale (finite,
-            // zeroed at the start) contents, every row masked.
+            // zeroed at the start) contents, every row masked.  A wave that
+            // holds no rows (possible in a head's last tile) skips every pair.
+            if (!wave_has_rows) return;
             const uint32_t mw0 = s_bits[UNW * s_ulist[i / nkb_cube] + wave];
             const uint32_t mw1 = two ? s_bits[UNW * s_ulist[(i + 1) / nkb_cube] + wave] : 0u;
             const bool sel0 = ((mw0 >> lr) & 1u) != 0u, sel1 = ((mw1 >> lr) & 1u) != 0u;
@@ -839,7 +821,8 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
         (m_run + __log2f(l_run)) * 0.69314718055994531f;
   uint16_t* dst;
   if (video) {
-    const int n = raster_of(g, c, pos - c * g.S);
+    const int cr = pos / g.S;
+    const int n = raster_of(g, cr, pos - cr * g.S);
     dst = (uint16_t*)a.out_raster + ((size_t)n * g.Hq + hq) * D;
   } else {
     dst = (uint16_t*)a.out_extra + ((size_t)pos * g.Hq + hq) * D;
@@ -858,7 +841,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
 template <int D>
 hipError_t launch_union(const AttnArgs& a, hipStream_t s) {
   USched sc;
-  sc.video_tiles_per_group = a.has_video ? (a.hg.gmax * a.g.S + UTR - 1) / UTR : 0;
+  sc.video_tiles_per_group = a.has_video ? (int)(((long)a.hg.gmax * a.g.N + UTR - 1) / UTR) : 0;
   sc.extra_tiles_per_group = a.extra_tiles_per_group;
   sc.extra_chunks = a.extra_chunks;
   sc.extra_chunk_cubes = a.extra_chunk_cubes;
@@ -867,10 +850,10 @@ hipError_t launch_union(const AttnArgs& a, hipStream_t s) {
   long video_blocks = 0;
   if (a.has_video) {
     if (sc.xcd_mode) {
-      const int stride_c = 8 / a.g.Hkv;
-      video_blocks = 8L * ((a.g.Nc + stride_c - 1) / stride_c) * sc.video_tiles_per_group;
+      const int per = 8 / a.g.Hkv;  // XCDs serving one KV head
+      video_blocks = 8L * ((sc.video_tiles_per_group + per - 1) / per);
     } else {
-      video_blocks = (long)a.g.Nc * a.g.Hkv * sc.video_tiles_per_group;
+      video_blocks = (long)a.g.Hkv * sc.video_tiles_per_group;
     }
   }
   const long blocks = sc.n_extra_wgs + video_blocks;
