@@ -114,6 +114,9 @@ __global__ __launch_bounds__(BNT, 1) void k_bwd_dq(BwdArgs a) {
   const int Nv = a.has_video ? g.N : 0;
 
   // ---- tile ----
+  // video tiles: 256 consecutive video rows of a KV head, numbered query cube
+  // by query cube from the last (head slot, offset), so a tile may span query
+  // cubes; each row's own cube joins its bitmap in the passes below
   bool video;
   int grp, rho0, c = 0;
   int b = blockIdx.x;
@@ -124,28 +127,32 @@ __global__ __launch_bounds__(BNT, 1) void k_bwd_dq(BwdArgs a) {
   } else {
     video = true;
     b -= a.n_extra_tiles;
-    const int per_c = g.Hkv * a.video_tiles_per_group;
-    c = g.Nc - 1 - b / per_c;
-    const int rem = b % per_c;
-    grp = rem / a.video_tiles_per_group;
-    rho0 = (rem - grp * a.video_tiles_per_group) * BTR;
+    grp = b % g.Hkv;
+    rho0 = (b / g.Hkv) * BTR;
   }
   const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
-  const int n_rows = min(BTR, (video ? gsz * g.S : gsz * a.n_extra) - rho0);
+  const int n_rows = min(BTR, (video ? gsz * g.N : gsz * a.n_extra) - rho0);
   if (n_rows <= 0) return;
   const int hstart = a.hg.start[grp];
+  if (video) c = g.Nc - 1 - rho0 / (gsz * g.S);  // the tile's highest query cube
   const int t_row = wave * 32 + lr;
   const bool row_ok = t_row < n_rows;
   int hq = 0, pos = 0;
   if (row_ok) {
     const int rho = rho0 + t_row;
-    const int per = video ? g.S : a.n_extra;
-    const int slot = rho / per;
-    hq = a.hg.heads[hstart + slot];
-    pos = video ? c * g.S + (rho - slot * g.S) : rho - slot * a.n_extra;
+    if (video) {
+      const int ci = rho / (gsz * g.S);
+      const int rem = rho - ci * gsz * g.S;
+      const int slot = rem / g.S;
+      hq = a.hg.heads[hstart + slot];
+      pos = (g.Nc - 1 - ci) * g.S + (rem - slot * g.S);
+    } else {
+      const int slot = rho / a.n_extra;
+      hq = a.hg.heads[hstart + slot];
+      pos = rho - slot * a.n_extra;
+    }
   }
   const int rr = video ? pos : Nv + pos;  // row index within the head
-  const bool wave_has_rows = wave * 32 < n_rows;
 
   // operands: Q^T and dO^T (row lr, d = 16*ds + 8*lh + [0..8)), row's log2 LSE and D
   bbf16x8 qb[D / 16], db[D / 16];
@@ -289,22 +296,18 @@ __global__ __launch_bounds__(BNT, 1) void k_bwd_dq(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
   };
 
-  // own cube (video rows)
-  if (video) {
-    walk(nkb, [&](int) { return c; },
-         [&](int, const uint16_t* kb, const uint16_t* vb, const uint16_t* tb) __attribute__((always_inline)) {
-           if (wave_has_rows) compute(kb, vb, tb, row_ok);
-         });
-  }
-  // selected cubes: passes of BPASS cubes over the word-major bitmap
-  const int cube_hi = video ? c : g.Nc;
+  // attended cubes (selected, and for video rows their own cubes): passes of
+  // BPASS cubes over the word-major bitmap
+  const int cube_hi = video ? c + 1 : g.Nc;
   const uint32_t* rbits = a.bits + (size_t)hq * a.W * R + rr;
+  const int own_c = (video && row_ok) ? pos / g.S : -1;  // not in the lists: added here
   for (int jb = 0; jb < cube_hi; jb += BPASS) {
     const int je = min(cube_hi, jb + BPASS);
     const int span = je - jb;
     __syncthreads();
     for (int w0 = jb >> 5; w0 < (je + 31) >> 5; ++w0) {
-      const uint32_t word = (row_ok && lh == 0) ? rbits[(size_t)w0 * R] : 0u;
+      uint32_t word = (row_ok && lh == 0) ? rbits[(size_t)w0 * R] : 0u;
+      if (lh == 0 && own_c >= 0 && (own_c >> 5) == w0) word |= 1u << (own_c & 31);
       for (int bit = 0; bit < 32; ++bit) {
         const int u = 32 * w0 + bit - jb;
         const uint32_t m = (uint32_t)__ballot((word >> bit) & 1u);
@@ -636,7 +639,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 void plan_backward(BwdArgs& a) {
   const KGeom& g = a.g;
   a.W = (g.Nc + 31) / 32;
-  a.video_tiles_per_group = a.has_video ? (a.hg.gmax * g.S + BTR - 1) / BTR : 0;
+  a.video_tiles_per_group = a.has_video ? (int)(((int64_t)a.hg.gmax * g.N + BTR - 1) / BTR) : 0;
   a.extra_tiles_per_group = a.n_extra ? (a.hg.gmax * a.n_extra + BTR - 1) / BTR : 0;
   a.n_extra_tiles = g.Hkv * a.extra_tiles_per_group;
   a.list_cap_g = (int64_t)a.hg.gmax * ((a.has_video ? (int64_t)g.S * g.Nc * (g.Nc + 1) / 2 : 0) +
@@ -674,13 +677,13 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   const int nkb = g.S / BKB;
   if (g.D == 128) {
     hipLaunchKernelGGL(k_bwd_prep<128>, dim3((rows + 15) / 16), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_bwd_dq<128>, dim3(a.n_extra_tiles + g.Nc * g.Hkv * a.video_tiles_per_group), dim3(BNT),
+    hipLaunchKernelGGL(k_bwd_dq<128>, dim3(a.n_extra_tiles + g.Hkv * a.video_tiles_per_group), dim3(BNT),
                        0, s, a);
     hipLaunchKernelGGL(k_bwd_lists, dim3(g.Hkv * g.Nc), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_bwd_dkdv<128>, dim3(g.Nc * g.Hkv * nkb), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(k_bwd_prep<64>, dim3((rows + 15) / 16), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_bwd_dq<64>, dim3(a.n_extra_tiles + g.Nc * g.Hkv * a.video_tiles_per_group), dim3(BNT),
+    hipLaunchKernelGGL(k_bwd_dq<64>, dim3(a.n_extra_tiles + g.Hkv * a.video_tiles_per_group), dim3(BNT),
                        0, s, a);
     hipLaunchKernelGGL(k_bwd_lists, dim3(g.Hkv * g.Nc), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_bwd_dkdv<64>, dim3(g.Nc * g.Hkv * nkb), dim3(256), 0, s, a);
