@@ -43,7 +43,8 @@ def test_tiny_f32(name):
 
 @pytest.mark.parametrize("p", [0.05, 0.7, 0.95])
 def test_small_bf16(p):
-    # 3 heads per KV group x 64 tokens = 192 rows per query cube: tiles of 128 + 64
+    # 3 heads per KV group x 64 tokens = 192 rows per query cube: 256-row tiles
+    # span two query cubes
     _case(SMALL, p=p)
 
 
@@ -59,6 +60,19 @@ def test_small_bf16_p1_is_dense_block_causal():
 def test_small_bf16_head_map_d64():
     wl = SMALL.replace(name="small_d64", head_dim=64, n_q_heads=5, seed=32)
     _case(wl, head_map=[1, 0, 1, 1, 0])
+
+
+@pytest.mark.parametrize("shape", ["s64_one_head_per_kv", "s128_one_head_per_kv"])
+def test_tiles_span_several_query_cubes(shape):
+    # one query head per KV head: 64 rows per query cube (a 256-row tile spans
+    # four cubes) or 128 rows with two key blocks per cube (two cubes per tile)
+    if shape == "s64_one_head_per_kv":
+        wl = workloads.Workload(name="span4", T=8, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=2,
+                                n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7, seed=41)
+    else:
+        wl = workloads.Workload(name="span2_s128", T=8, H=16, W=16, ct=2, ch=8, cw=8, n_q_heads=3,
+                                n_kv_heads=3, head_dim=128, dtype="bf16", p=0.6, seed=42)
+    _case(wl)
 
 
 def test_text_rows_causal_s128():
