@@ -670,7 +670,7 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // own cube is one more bit of the same bitmap
   const int my_row = tid >> 1, my_half = tid & 1;
   const int32_t* my_list = nullptr;
-  int my_cnt = 0, my_c = -1;
+  int my_cnt = 0, my_c = -1, my_lo = 0;
   if (video && my_row < n_rows) {
     const int rho = rho0 + my_row;
     const int ci = rho / (gsz * g.S);
@@ -717,11 +717,18 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     }
     __syncthreads();
     if (video && my_row < n_rows) {
-      // entries in [jb, je): binary search for both ends (lists are ascending)
-      int lo = 0, hi = my_cnt;
-      while (lo < hi) { const int mid = (lo + hi) >> 1; if (my_list[mid] < jb) lo = mid + 1; else hi = mid; }
-      int lo2 = lo, hi2 = my_cnt;
-      while (lo2 < hi2) { const int mid = (lo2 + hi2) >> 1; if (my_list[mid] < je) lo2 = mid + 1; else hi2 = mid; }
+      // entries in [lo, lo2) lie in [jb, je) (lists are ascending).  Every
+      // entry is below cube_hi and at least cube_lo = 0, and passes run
+      // downwards, so a bound needs a binary search (dependent loads from
+      // global memory) only inside the cube range: the upper one is the
+      // previous pass's lower one.
+      const int lo2 = je == cube_hi ? my_cnt : my_lo;
+      int lo = 0;
+      if (jb > cube_lo) {
+        int hi = lo2;
+        while (lo < hi) { const int mid = (lo + hi) >> 1; if (my_list[mid] < jb) lo = mid + 1; else hi = mid; }
+      }
+      my_lo = lo;
       const uint32_t bit = 1u << (my_row & 31);
       uint32_t* wbase = &s_bits[my_row >> 5];
 #pragma unroll 4
