@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ: union tiles of 256 rows sharing a KV head (extra rows first, then video
-// tiles by descending query cube)
+// tiles of consecutive rows from the last query cube down)
 // ---------------------------------------------------------------------------
 template <int D>
 struct BSmem {
