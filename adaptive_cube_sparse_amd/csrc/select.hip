@@ -110,18 +110,18 @@ bool use_split_select(const KGeom& g, int n_extra, int gmax) {
 // (capacity 64 * NPL), NW waves that share every kbar load across RT rows.
 // Bands whose logits fill most of the LDS (one workgroup per CU) take 16
 // waves, so that each SIMD still holds four of them.
+// Tile b of a band (sZ: RT * 64 * NPL floats of LDS).
 template <int D, int RT, int NPL, int NW>
-__global__ __launch_bounds__(64 * NW) void k_select_bf16(SelectArgs a, TileSched ts) {
+__device__ __forceinline__ void select_tile(const SelectArgs& a, const TileSched& ts, int b, float* sZ) {
   constexpr int NCAP = kWave * NPL;
   constexpr int RB = (RT + 15) / 16;  // 16-row MFMA blocks
-  __shared__ float sZ[RT * NCAP];
   const KGeom& g = a.g;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
 
   int grp, n, rho0;
   bool video;
-  decode_tile(blockIdx.x, ts, g.Hkv, g.Nc, RT, grp, n, rho0, video);
+  decode_tile(b, ts, g.Hkv, g.Nc, RT, grp, n, rho0, video);
   // n == candidate count: c for a video row in cube c, Nc for extra rows.
   const int gsz = a.hg.start[grp + 1] - a.hg.start[grp];
   const int group_rows = video ? gsz * g.S : gsz * a.n_extra;
@@ -226,6 +226,46 @@ __global__ __launch_bounds__(64 * NW) void k_select_bf16(SelectArgs a, TileSched
       cnt = topp_select_row<NPL>(E, n, zs, a.p, a.sel_idx + off, &sZ[row * NCAP]);
     }
     if (lane == 0) a.sel_count[(size_t)rr.hq * a.rows_per_head + row_index] = cnt;
+  }
+}
+
+// One band per launch.
+template <int D, int RT, int NPL, int NW>
+__global__ __launch_bounds__(64 * NW) void k_select_bf16(SelectArgs a, TileSched ts) {
+  __shared__ float sZ[RT * kWave * NPL];
+  select_tile<D, RT, NPL, NW>(a, ts, blockIdx.x, sZ);
+}
+
+// Several bands of 32-row tiles with one workgroup size in one launch, so the
+// partly filled last round of each band's workgroups overlaps the next band
+// instead of leaving CUs idle; the LDS holds the largest band's logits.
+// NW = 16: the 768 and 1024-candidate bands; NW = 8: bands of at most 384.
+constexpr int kMaxBands = 4;
+struct BandSet {
+  TileSched ts[kMaxBands];
+  int npl[kMaxBands];
+  int first[kMaxBands + 1];  // first workgroup of each band; first[n] = total
+  int n;
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_select_bands(SelectArgs a, BandSet bs) {
+  constexpr int MAXNPL = NW == 16 ? 16 : 6;
+  __shared__ float sZ[32 * kWave * MAXNPL];
+  const int b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < bs.n && b >= bs.first[i + 1]) ++i;
+  const int lb = b - bs.first[i];
+  if constexpr (NW == 16) {
+    if (bs.npl[i] == 16) select_tile<D, 32, 16, 16>(a, bs.ts[i], lb, sZ);
+    else select_tile<D, 32, 12, 16>(a, bs.ts[i], lb, sZ);
+  } else {
+    switch (bs.npl[i]) {
+      case 6: select_tile<D, 32, 6, 8>(a, bs.ts[i], lb, sZ); break;
+      case 4: select_tile<D, 32, 4, 8>(a, bs.ts[i], lb, sZ); break;
+      case 2: select_tile<D, 32, 2, 8>(a, bs.ts[i], lb, sZ); break;
+      default: select_tile<D, 32, 1, 8>(a, bs.ts[i], lb, sZ); break;
+    }
   }
 }
 
@@ -628,9 +668,9 @@ __global__ __launch_bounds__(256) void k_select_f32(SelectArgs a, int total_vide
 
 // One launch serves video query cubes [c_lo, c_hi) and, if with_extra, the
 // extra rows (which have Nc candidates).
-template <int D, int RT, int NPL, int NW>
-static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, bool with_extra) {
-  TileSched ts;
+// Tiles of RT rows for video query cubes [c_lo, c_hi) and, if with_extra, the
+// extra rows; returns the workgroup count.
+static int band_sched(const SelectArgs& a, int RT, int c_lo, int c_hi, bool with_extra, TileSched& ts) {
   const int gmax = a.hg.gmax;
   ts.video_tiles_per_group = a.has_video ? (gmax * a.g.S + RT - 1) / RT : 0;
   ts.extra_tiles_per_group = (with_extra && a.n_extra) ? (gmax * a.n_extra + RT - 1) / RT : 0;
@@ -638,9 +678,33 @@ static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, 
   ts.c_lo = c_lo;
   ts.c_hi = c_hi;
   const int nc = a.has_video && c_hi > c_lo ? c_hi - c_lo : 0;
-  const int blocks = ts.n_extra_tiles + nc * a.g.Hkv * ts.video_tiles_per_group;
+  return ts.n_extra_tiles + nc * a.g.Hkv * ts.video_tiles_per_group;
+}
+
+template <int D, int RT, int NPL, int NW>
+static void launch_bf16(const SelectArgs& a, hipStream_t s, int c_lo, int c_hi, bool with_extra) {
+  TileSched ts;
+  const int blocks = band_sched(a, RT, c_lo, c_hi, with_extra, ts);
   if (blocks > 0)
     hipLaunchKernelGGL((k_select_bf16<D, RT, NPL, NW>), dim3(blocks), dim3(64 * NW), 0, s, a, ts);
+}
+
+// Adds band (npl, c_lo, c_hi, with_extra) of 32-row tiles to a band set.
+static void add_band(const SelectArgs& a, BandSet& bs, int npl, int c_lo, int c_hi, bool with_extra) {
+  TileSched ts;
+  const int blocks = band_sched(a, 32, c_lo, c_hi, with_extra, ts);
+  if (blocks <= 0) return;
+  if (bs.n == 0) bs.first[0] = 0;
+  bs.ts[bs.n] = ts;
+  bs.npl[bs.n] = npl;
+  bs.first[bs.n + 1] = bs.first[bs.n] + blocks;
+  ++bs.n;
+}
+
+template <int D, int NW>
+static void launch_bands(const SelectArgs& a, hipStream_t s, const BandSet& bs) {
+  if (bs.n > 0)
+    hipLaunchKernelGGL((k_select_bands<D, NW>), dim3(bs.first[bs.n]), dim3(64 * NW), 0, s, a, bs);
 }
 
 // Video rows of query cube c have c candidates; split them by capacity so
@@ -657,15 +721,20 @@ static void launch_bf16_all(const SelectArgs& a, hipStream_t s) {
     const bool ex = extra && Nc > lo && Nc <= hi;
     if (h > l || ex) launch(l, h, ex);
   };
+  BandSet big{}, small{};
   band([&](int l, int h, bool ex) { launch_bf16<D, 8, 64, 16>(a, s, l, h, ex); }, 2048, 4096);
   band([&](int l, int h, bool ex) { launch_bf16<D, 16, 32, 16>(a, s, l, h, ex); }, 1024, 2048);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 16, 16>(a, s, l, h, ex); }, 768, 1024);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 12, 16>(a, s, l, h, ex); }, 512, 768);
+  band([&](int l, int h, bool ex) { add_band(a, big, 16, l, h, ex); }, 768, 1024);
+  band([&](int l, int h, bool ex) { add_band(a, big, 12, l, h, ex); }, 512, 768);
+  launch_bands<D, 16>(a, s, big);
+  // 512 candidates (64 KB of logits, two workgroups per CU) alone: with the
+  // smaller bands it would lower their occupancy
   band([&](int l, int h, bool ex) { launch_bf16<D, 32, 8, 8>(a, s, l, h, ex); }, 384, 512);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 6, 8>(a, s, l, h, ex); }, 256, 384);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 4, 8>(a, s, l, h, ex); }, 128, 256);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 2, 8>(a, s, l, h, ex); }, 64, 128);
-  band([&](int l, int h, bool ex) { launch_bf16<D, 32, 1, 8>(a, s, l, h, ex); }, 0, 64);
+  band([&](int l, int h, bool ex) { add_band(a, small, 6, l, h, ex); }, 256, 384);
+  band([&](int l, int h, bool ex) { add_band(a, small, 4, l, h, ex); }, 128, 256);
+  band([&](int l, int h, bool ex) { add_band(a, small, 2, l, h, ex); }, 64, 128);
+  band([&](int l, int h, bool ex) { add_band(a, small, 1, l, h, ex); }, 0, 64);
+  launch_bands<D, 8>(a, s, small);
   if (split) {
     // split path for the extra rows (workspace holds their logits)
     hipLaunchKernelGGL((k_select_scores<D>), dim3((Nc + 63) / 64, a.g.Hkv), dim3(256), 0, s, a);
