@@ -119,6 +119,16 @@ def test_many_cubes_small_cube():
     _case(wl, rows="sample", cubes_per_decile=3, tokens_per_cube=8)
 
 
+def test_extra_rows_with_video_bands_in_one_launch():
+    # Nc = 320: the extra rows' 320 candidates and the video rows of cubes
+    # 256..319 share the 6-slot band, and the 4-, 2- and 1-slot bands of the
+    # earlier cubes run in the same selection launch at their own offsets
+    wl = workloads.Workload(name="bands_extra", T=20, H=16, W=16, ct=1, ch=4, cw=4,
+                            n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7,
+                            seed=41, n_decode=6)
+    _case(wl, rows="sample", cubes_per_decile=3, tokens_per_cube=8)
+
+
 def test_deterministic():
     data = workloads.generate(SMALL)
     a = run_device(SMALL, data)
