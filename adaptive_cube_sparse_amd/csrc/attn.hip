@@ -207,9 +207,11 @@ void plan_attention(AttnArgs& a, adas_dtype dt) {
   a.decode_chunks = 0;
   a.bits_words = (a.g.Nc + 31) / 32;
   if (dt != ADAS_BF16 || a.n_extra == 0) return;
-  if (!a.has_video && a.hg.gmax * a.n_extra <= 32 && a.g.S % 64 == 0) {
+  if (!a.has_video && a.n_text_kv == 0 && a.hg.gmax * a.n_extra <= 32 && a.g.S % 64 == 0) {
     // decode mode: k_attn_decode, one workgroup per (KV head, chunk), about one
-    // per CU; each chunk leaves one partial row per extra row
+    // per CU; each chunk leaves one partial row per extra row.  The decode
+    // kernel reads no text keys, so a text prefill (causal text keys) always
+    // takes the union tiles, which attend the text keys in chunk 0.
     const int want = (256 + a.g.Hkv - 1) / a.g.Hkv;
     int cubes = (a.g.Nc + want - 1) / want;
     cubes = ((cubes + decode_waves() - 1) / decode_waves()) * decode_waves();

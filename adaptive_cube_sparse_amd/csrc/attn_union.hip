@@ -609,9 +609,14 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
     issue_block(2, C2{});
     issue_block(3, C3{});
     auto pair = [&](auto b0, auto b1, auto n0, auto n1, int i) __attribute__((always_inline)) {
-      // blocks i, i+1 have landed (blocks i+2, i+3 may still be in flight at i = 0)
-      if (i == 0 && nb > 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NLMIN));
-      else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      // blocks i, i+1 must have landed.  At i = 0 the loads of blocks 2 and 3
+      // (those that exist) may stay in flight: a wave issues NLMIN or NLMIN+1
+      // loads per block and loads complete in order, so allowing 2*NLMIN
+      // pending loads (two blocks behind) or NLMIN (one block behind, nb == 3)
+      // still covers every load of blocks 0 and 1.
+      if (i == 0 && nb > 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLMIN));
+      else if (i == 0 && nb == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLMIN));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (i >= 2) {
         issue_block(i + 2, n0);
