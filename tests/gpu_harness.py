@@ -19,7 +19,7 @@ import torch
 
 import workloads
 from oracle import adas_oracle as O
-from oracle.compare import grade_row, grade_row_topk
+from oracle.compare import grade_row, grade_row_topk, logit_error_bound
 
 TOL_BF16 = (2e-2, 2e-3)   # max-abs, mean-abs
 TOL_F32 = (1e-4, 1e-5)
@@ -151,31 +151,43 @@ def fetch_lists(ref: Reference, layer, rows):
 
 
 def selection_probs(ref: Reference, kind, hq, i):
+    """(P, z, bound) of a row: float64 probabilities and logits over its
+    candidates, and the float32 scoring error bound of each logit."""
     kb = ref.kbar[ref.kv(hq)]
     if kind == "v":
         c = i // ref.g.S
         q = O.to_f64(ref.q_cube[hq, i])
-        return O.selection_probabilities(q, kb[:c])
-    q = O.to_f64(ref.data["q_text"][i, hq])
-    return O.selection_probabilities(q, kb)
+        kb = kb[:c]
+    else:
+        q = O.to_f64(ref.data["q_text"][i, hq])
+    z = O.selection_logits(q, kb)
+    return O.softmax(z), z, logit_error_bound(q, kb, z)
 
 
-def check_rows(ref: Reference, layer, rows, p, max_mismatch_frac=0.01, k=None):
+# Regression alarm, not a correctness bar (every non-exact row is justified on
+# its own by the grader): near-tie rows need a cut gap inside the float32
+# scoring error, which is about 1e-6 in a logit on these inputs, so they are
+# expected in well under 0.1% of rows; near-threshold rows (within 1e-5 of p)
+# in about 0.2%.
+ALARM_FRAC = 0.01
+
+
+def check_rows(ref: Reference, layer, rows, p, k=None):
     """Grade the selection of `rows` (Top-p, or Top-k when k is given) and
     compare their outputs."""
     lists = fetch_lists(ref, layer, rows)
     grades = {"exact": 0, "near_threshold": 0, "near_tie": 0, "fail": 0}
     fails = []
     for (kind, hq, i), S in zip(rows, lists):
-        P = selection_probs(ref, kind, hq, i)
-        gr = grade_row(P, p, S) if k is None else grade_row_topk(P, k, S)
+        P, z, bnd = selection_probs(ref, kind, hq, i)
+        gr = grade_row(P, p, S, z, bnd) if k is None else grade_row_topk(P, k, S, z, bnd)
         grades[gr] += 1
         if gr == "fail" and len(fails) < 5:
             want = O.top_p(P, p) if k is None else O.top_k(P, k)
             fails.append((kind, hq, i, S[:10].tolist(), want[:10].tolist()))
     log(f"  selection grades over {len(rows)} rows: {grades}")
     assert grades["fail"] == 0, f"selection failures: {fails}"
-    assert grades["near_threshold"] + grades["near_tie"] <= max(2, max_mismatch_frac * len(rows))
+    assert grades["near_threshold"] + grades["near_tie"] <= max(2, ALARM_FRAC * len(rows))
     # outputs, with the oracle attending over the device's (validated) sets
     wl = ref.wl
     out_r = bits(layer.out_raster) if layer.out_raster is not None else None
