@@ -75,6 +75,16 @@ def test_tiles_span_several_query_cubes(shape):
     _case(wl)
 
 
+def test_cubes_of_256_tokens():
+    # the training cube of the listing's Table 5, 8x8x4 (h x w x t): four key
+    # blocks per cube, 7 query heads per KV head (1792 rows per query cube,
+    # so tiles span cube boundaries mid-head), plus text rows
+    wl = workloads.Workload(name="cube256", T=16, H=16, W=16, ct=4, ch=8, cw=8, n_q_heads=7,
+                            n_kv_heads=1, head_dim=128, dtype="bf16", p=0.8, seed=46,
+                            n_text=20, text_kv=True)
+    _case(wl)
+
+
 def test_text_rows_causal_s128():
     # cube 8x8x2 = 128 tokens (two key blocks per cube) + 70 causal text tokens
     wl = workloads.Workload(name="text", T=8, H=16, W=16, ct=2, ch=8, cw=8, n_q_heads=4,
@@ -127,6 +137,29 @@ def test_extra_rows_with_video_bands_in_one_launch():
                             n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7,
                             seed=41, n_decode=6)
     _case(wl, rows="sample", cubes_per_decile=3, tokens_per_cube=8)
+
+
+def test_three_block_passes():
+    # 3 cubes of 64 tokens, 4 query heads on one KV head: a tile is one query
+    # cube (256 rows), so the tile of cube 2 walks exactly three key blocks
+    # (own cube 2 plus cubes 1 and 0 whenever a row selects them), the case
+    # where the first wait of the four-buffer pipeline has only one block
+    # still loading behind the pair it computes
+    wl = workloads.Workload(name="three_blocks", T=12, H=4, W=4, ct=4, ch=4, cw=4, n_q_heads=4,
+                            n_kv_heads=1, head_dim=128, dtype="bf16", p=0.95, seed=43)
+    _case(wl)
+    wl = wl.replace(name="three_blocks_d64", head_dim=64, p=0.9, seed=44)
+    _case(wl)
+
+
+def test_text_prefill_without_video_rows():
+    # a few text queries with causal text keys and no video rows: at most 32
+    # rows per KV head, which is the decode kernel's size, but the decode
+    # kernel reads no text keys, so these rows must take the union tiles
+    wl = workloads.Workload(name="text_only", T=16, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=4,
+                            n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7, seed=45,
+                            video_queries=False, n_text=6, text_kv=True)
+    _case(wl)
 
 
 def test_deterministic():
