@@ -32,6 +32,7 @@ EXPORTS = (
     "adas_status_string", "adas_last_error", "adas_version",
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd",
+    "adas_probe_mfma", "adas_probe_hbm_read", "adas_probe_hbm_copy",
 )
 
 
@@ -88,6 +89,9 @@ def load() -> ctypes.CDLL:
                                            vp, vp, vp, sz, vp]),
         "adas_sparse_attn_bwd": (i32, [gp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]),
+        "adas_probe_mfma": (i32, [i32, i32, vp, ctypes.POINTER(f64), vp]),
+        "adas_probe_hbm_read": (i32, [vp, i64, vp, i32, vp]),
+        "adas_probe_hbm_copy": (i32, [vp, vp, i64, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -400,6 +404,42 @@ def adas_sel_capacity(geom: Geometry, has_video: bool, n_extra: int) -> int:
 
 def adas_version() -> str:
     return load().adas_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# measurement helpers (peak probes; not part of the method)
+# ---------------------------------------------------------------------------
+def adas_probe_mfma(workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch the MFMA-only loop; returns the dense bf16 FLOPs it issues."""
+    lib = load()
+    _shape(sink, (workgroups,), "sink")
+    fl = ctypes.c_double(0.0)
+    st = lib.adas_probe_mfma(int(workgroups), int(iters), _ptr(sink, torch.float32, "sink"), ctypes.byref(fl),
+                             _stream(stream))
+    _check(st, "adas_probe_mfma")
+    return fl.value
+
+
+def adas_probe_hbm_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, stream=None) -> int:
+    """Stream src once; returns the bytes read."""
+    lib = load()
+    nbytes = src.numel() * src.element_size()
+    st = lib.adas_probe_hbm_read(_ptr(src, name="src"), nbytes, _ptr(sink, torch.int32, "sink"), int(workgroups),
+                                 _stream(stream))
+    _check(st, "adas_probe_hbm_read")
+    return nbytes
+
+
+def adas_probe_hbm_copy(src: torch.Tensor, dst: torch.Tensor, workgroups: int = 0, stream=None) -> int:
+    """Copy src to dst; returns the bytes copied (each way)."""
+    lib = load()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    st = lib.adas_probe_hbm_copy(_ptr(src, name="src"), _ptr(dst, name="dst"), nbytes, int(workgroups),
+                                 _stream(stream))
+    _check(st, "adas_probe_hbm_copy")
+    return nbytes
 
 
 # ---------------------------------------------------------------------------

@@ -506,4 +506,28 @@ const char* adas_last_error(void) { return g_last_error; }
 
 const char* adas_version(void) { return "0.1"; }
 
+adas_status adas_probe_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream) {
+  if (workgroups < 1 || iters < 1) return fail(ADAS_ERR_VALUE, "workgroups and iters must be >= 1");
+  if (sink == nullptr) return fail(ADAS_ERR_NULL, "sink is NULL");
+  if (flops != nullptr) *flops = adas::probe_mfma_flops_per_wg(iters) * workgroups;
+  return hip_status(adas::launch_probe_mfma(workgroups, iters, sink, (hipStream_t)stream), "adas_probe_mfma launch");
+}
+
+adas_status adas_probe_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                                void* stream) {
+  if (src == nullptr || sink == nullptr) return fail(ADAS_ERR_NULL, "src/sink is NULL");
+  if (bytes <= 0 || bytes % 16) return fail(ADAS_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (workgroups < 1) workgroups = 8 * 256;
+  return hip_status(adas::launch_probe_read(src, bytes, sink, workgroups, (hipStream_t)stream),
+                    "adas_probe_hbm_read launch");
+}
+
+adas_status adas_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32_t workgroups, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(ADAS_ERR_NULL, "src/dst is NULL");
+  if (bytes <= 0 || bytes % 16) return fail(ADAS_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (workgroups < 1) workgroups = 8 * 256;
+  return hip_status(adas::launch_probe_copy(src, dst, bytes, workgroups, (hipStream_t)stream),
+                    "adas_probe_hbm_copy launch");
+}
+
 }  // extern "C"

@@ -419,4 +419,10 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t s);
 int decode_waves();     // waves per workgroup of the decode kernel
 int decode_max_chunk_cubes();  // most cubes in one chunk of the decode kernel
 
+// peak probes (probe.hip)
+double probe_mfma_flops_per_wg(int iters);
+hipError_t launch_probe_mfma(int wgs, int iters, float* sink, hipStream_t s);
+hipError_t launch_probe_read(const void* src, long bytes, uint32_t* sink, int wgs, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, long bytes, int wgs, hipStream_t s);
+
 }  // namespace adas

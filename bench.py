@@ -48,7 +48,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "AdaS-Attn effective TFLOP/s (selected tokens) and % of MI355X bf16/HBM peak"
-DEFAULT_WORKLOAD = "qwen3b"
+DEFAULT_WORKLOAD = "hour"
 
 
 def parse():
@@ -69,6 +69,10 @@ def parse():
                     help="decode tokens per step for the decode workload (1 = one step)")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward of the sparse attention (selection held fixed)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the peak probes (MFMA-only loop, HBM read and copy streams)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="decode: do not flush the caches between steps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -209,7 +213,7 @@ def decode_unique_bytes(layer, wl) -> int:
     return kv_bytes + qo + list_entries * 4 + Hq * n_extra * 4
 
 
-def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict) -> dict:
+def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict, probes=None) -> dict:
     """Each step of the path against the MI355X peak that bounds it: the
     cube gather (partition of Q, K, V: every element read and written once,
     plus perm) and the mean-key reduction (K read, float32 mean keys written)
@@ -242,10 +246,140 @@ def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict) -> dict:
                      "bound": "alu (Top-p search; the scoring product is a small share)"}
     out["attention"] = {"ms": roof["launch_ms"], "bound": roof["bound"], "achieved": roof["achieved"],
                         "unit": roof["unit"], "frac": roof["frac"]}
+    if probes:
+        for k in ("gather", "mean_keys"):
+            if k in out:
+                out[k]["frac_of_measured"] = out[k]["GB/s"] / probes["hbm_copy_GB/s" if k == "gather" else
+                                                                       "hbm_read_GB/s"]
+        out["select"]["scoring_frac_of_measured"] = t / probes["mfma_bf16_TFLOP/s"]
+        ref = probes["mfma_bf16_TFLOP/s"] if roof["unit"] == "TFLOP/s" else probes["hbm_read_GB/s"]
+        out["attention"]["frac_of_measured"] = roof["achieved"] / ref
     return out
 
 
-def cpu_baseline(wl, data, budget_s: float, topk: int = 0):
+def peak_probes() -> dict:
+    """Measured ceilings: an MFMA-only register loop (dense bf16) and
+    streaming HBM reads / copies of 2 GiB (far beyond the 256 MB of on-die
+    caches), each timed with HIP events, best of three."""
+    import torch
+    from adaptive_cube_sparse_amd._lib import adas_probe_hbm_copy, adas_probe_hbm_read, adas_probe_mfma
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def best(fn, reps=3):
+        out = []
+        for _ in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3)
+        return min(out[1:])
+
+    wgs = 2048
+    sink = torch.zeros(wgs, dtype=torch.float32, device=dev)
+    fl = [0.0]
+
+    def mf():
+        fl[0] = adas_probe_mfma(wgs, 2000, sink)
+    t = best(mf)
+    mfma = fl[0] / t / 1e12
+    n = 2 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    isink = torch.zeros(8 * 256, dtype=torch.int32, device=dev)
+    t_r = best(lambda: adas_probe_hbm_read(src, isink))
+    t_c = best(lambda: adas_probe_hbm_copy(src, dst))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_TFLOP/s": mfma, "hbm_read_GB/s": n / t_r / 1e9, "hbm_copy_GB/s": 2 * n / t_c / 1e9,
+            "note": "MFMA-only register loop (2048 workgroups x 4 waves x 4 chains); 2 GiB streams; "
+                    "best of 3, HIP events"}
+
+
+def selection_stats(layer, wl) -> dict:
+    """What the pages' Figure 4 plots per layer (cubes selected per query),
+    from the device lists: mean and quantiles of the selected count, a
+    10-bin histogram of the selected fraction of each row's candidates, and
+    per-row entropy is not computed (the lists do not carry P)."""
+    import torch
+    S = wl.cube_size
+    Nc = wl.n_tokens // S
+    cnt = layer.sel_count.to(torch.float64)
+    nv = wl.n_tokens if wl.video_queries else 0
+    fr = []
+    if nv:
+        cand = (torch.arange(nv, device=cnt.device) // S).to(torch.float64)
+        keep = cand > 0
+        fr.append((cnt[:, :nv] / cand.clamp_min(1))[:, keep].reshape(-1))
+    if cnt.shape[1] > nv:
+        fr.append((cnt[:, nv:] / Nc).reshape(-1))
+    f = torch.cat(fr)
+    hist = torch.histc(f, bins=10, min=0.0, max=1.0).to(torch.int64).tolist()
+    c_all = cnt.reshape(-1)
+    q = torch.quantile(c_all[: min(c_all.numel(), 1 << 24)], torch.tensor([0.5, 0.9, 0.99], dtype=torch.float64,
+                                                                           device=cnt.device)).tolist()
+    out = {"rows": int(c_all.numel()), "mean_cubes_per_row": float(c_all.mean().item()),
+           "p50_p90_p99_cubes": q, "max_cubes": int(c_all.max().item()),
+           "selected_fraction_hist": {"edges": [i / 10 for i in range(11)], "counts": hist},
+           "mean_selected_fraction": float(f.mean().item())}
+    if nv:
+        out["video_mean_selected_fraction"] = float(fr[0].mean().item())
+    if cnt.shape[1] > nv:
+        out["extra_mean_selected_fraction"] = float(fr[-1].mean().item())
+    return out
+
+
+def grade_sample(layer, wl, sample, topk: int = 0) -> dict:
+    """Grade the device's lists of the rows the CPU baseline sampled against
+    the oracle (exact / within 1e-5 of p / inside the float32 tie window /
+    fail), and count the sampled rows whose oracle sum lies within 1e-5 of p."""
+    import torch
+    from oracle.compare import TOL_MASS, grade_row, grade_row_topk, logit_error_bound
+    g = layer.geom
+    S, Nc, Hq = g.S, g.n_cubes, g.n_q_heads
+    capv = S * Nc * (Nc - 1) // 2 if wl.video_queries else 0
+    nv = g.N if wl.video_queries else 0
+    n_extra = wl.n_text + wl.n_decode
+    cnt = layer.sel_count.cpu().numpy()
+    offs, lens = [], []
+    for kind, hq, i, *_ in sample:
+        if kind == "v":
+            c, r = divmod(i, S)
+            offs.append(hq * capv + S * c * (c - 1) // 2 + r * c)
+            lens.append(int(cnt[hq, i]))
+        else:
+            offs.append(Hq * capv + (hq * n_extra + i) * Nc)
+            lens.append(int(cnt[hq, nv + i]))
+    if not sample:
+        return {}
+    L = max(max(lens), 1)
+    idx = torch.tensor(offs, dtype=torch.int64, device=layer.sel_idx.device)[:, None] + \
+        torch.arange(L, device=layer.sel_idx.device)[None, :]
+    got = layer.sel_idx[idx.clamp_max(layer.sel_idx.numel() - 1)].cpu().numpy()
+    grades = {"exact": 0, "near_threshold": 0, "near_tie": 0, "fail": 0}
+    near = 0
+    for j, (kind, hq, i, q, kb) in enumerate(sample):
+        z = (kb @ q) / np.sqrt(q.shape[0])
+        e = np.exp(z - z.max()) if len(z) else z
+        P = e / e.sum() if len(z) else z
+        Sd = got[j, :lens[j]]
+        b = logit_error_bound(q, kb, z)
+        gr = grade_row_topk(P, topk, Sd, z, b) if topk else grade_row(P, wl.p, Sd, z, b)
+        grades[gr] += 1
+        if not topk and len(P) and wl.p < 1.0:
+            cum = np.cumsum(np.sort(P)[::-1])
+            k = int(np.searchsorted(cum, wl.p, side="left")) + 1
+            k = min(k, len(P))
+            s_k, s_km1 = cum[k - 1], (cum[k - 2] if k >= 2 else 0.0)
+            near += int(abs(s_k - wl.p) <= TOL_MASS or abs(s_km1 - wl.p) <= TOL_MASS)
+    return {"rows": len(sample), "grades": grades, "oracle_rows_within_1e-5_of_p": near,
+            "note": "device lists of the CPU baseline's sampled rows graded against the oracle"}
+
+
+def cpu_baseline(wl, data, budget_s: float, topk: int = 0, sample_out=None):
     """Time the CPU oracle on a bounded, seeded sample of the workload's rows:
     selection softmax + Top-p + attention per row (partition and mean keys of
     the whole input are timed too).  BLAS is pinned to one thread."""
@@ -274,12 +408,16 @@ def cpu_baseline(wl, data, budget_s: float, topk: int = 0):
                 S_ = O.top_k(P, topk) if topk else O.top_p(P, wl.p)
                 O.attention_video_row(q_cube, k_cube, v_cube, g, hq, pos, S_)
                 keys = (len(S_) + 1) * g.S
+                if sample_out is not None:
+                    sample_out.append(("v", hq, pos, O.to_f64(q_cube[hq, pos]), kbar[hq // rep][:c]))
             else:
                 m = int(rng.integers(wl.n_decode or wl.n_text))
                 P = O.selection_probabilities(O.to_f64(data["q_text"][m, hq]), kbar[hq // rep])
                 S_ = O.top_k(P, topk) if topk else O.top_p(P, wl.p)
                 O.attention_extra_row(data["q_text"], k_cube, v_cube, g, hq, m, S_)
                 keys = len(S_) * g.S
+                if sample_out is not None:
+                    sample_out.append(("x", hq, m, O.to_f64(data["q_text"][m, hq]), kbar[hq // rep]))
             t_rows += time.perf_counter() - t1
             flops += 4.0 * wl.head_dim * keys
             rows += 1
@@ -528,12 +666,14 @@ def main():
 
     wl = workloads.get(args.config)
     decode = not wl.video_queries
+    dev = torch.device("cuda:0")
+    probes = None if args.no_probes else peak_probes()
+    t_gen = time.perf_counter()
+    data = workloads.generate(wl)   # decode: all of the workload's decode queries
+    t_gen = time.perf_counter() - t_gen
+    n_queries = wl.n_decode
     if decode:
         wl = wl.replace(n_decode=args.decode_batch)
-    dev = torch.device("cuda:0")
-    t_gen = time.perf_counter()
-    data = workloads.generate(wl)
-    t_gen = time.perf_counter() - t_gen
 
     def up(x):
         if x.dtype == np.uint16:
@@ -549,6 +689,19 @@ def main():
     q = up(data["q"]) if wl.video_queries else None
     k, v = up(data["k"]), up(data["v"])
     qe = up(data["q_text"]) if n_extra else None
+    qe_all = qe
+    if decode:
+        # each step decodes new query tokens: step i takes tokens
+        # (i * batch .. i * batch + batch) mod the workload's count
+        qe_all = up(data["q_text"])
+        nb = max(1, n_queries // args.decode_batch)
+        qe_steps = [qe_all[(i % nb) * args.decode_batch:(i % nb + 1) * args.decode_batch].contiguous()
+                    for i in range(nb)]
+        qe = qe_steps[0]
+    flush = None
+    if decode and not args.no_flush:
+        # 512 MiB written between decode steps evicts L2 and the memory-side cache
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     kt = up(data["k_text"]) if n_text_kv else None
     vt = up(data["v_text"]) if n_text_kv else None
     stream = torch.cuda.current_stream()
@@ -583,15 +736,23 @@ def main():
         ev["gather"].append((lay[0], lay[1]))
         ev["mean_keys"].append((lay[1], lay[2]))
 
-    def step(record):
+    used_queries = []
+
+    def step(record, i=0):
         e0 = e1 = None
+        q_i = qe
         if not decode:
             e0, e1, e2 = layout(record)
         else:
+            q_i = qe_steps[i % len(qe_steps)]
+            if record:
+                used_queries.append(i % len(qe_steps))
+            if flush is not None:
+                flush.zero_()
             e2 = mark() if record else None
-        layer.select(qe)
+        layer.select(q_i)
         e3 = mark() if record else None
-        layer.attend(qe, kt, vt)
+        layer.attend(q_i, kt, vt)
         e4 = mark() if record else None
         if record:
             if not decode:
@@ -601,28 +762,43 @@ def main():
             ev["select"].append((e2, e3))
             ev["attention"].append((e3, e4))
 
-    for _ in range(args.warmup):
-        step(False)
+    for i in range(args.warmup):
+        step(False, i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step(True, args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+    wall_ms_step = ms_step
 
     def mean_ms(pairs):
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
 
     k_ms = {name: mean_ms(p) for name, p in ev.items() if p and name in ("layout", "select", "attention")}
     st_ms = {name: mean_ms(p) for name, p in ev.items() if p}
-    pairs = attended_pairs(layer, wl)
+    if decode and flush is not None:
+        # the cache flush between steps is not part of a decode step: the step
+        # time is the event-timed selection + attention of each step
+        ms_step = k_ms["select"] + k_ms["attention"]
+    if decode:
+        # every decode query the timed steps used, counted as often as used
+        pairs_q, bytes_q = {}, {}
+        for j in sorted(set(used_queries)):
+            layer.select(qe_steps[j])
+            torch.cuda.synchronize()
+            pairs_q[j] = attended_pairs(layer, wl)
+            bytes_q[j] = decode_unique_bytes(layer, wl)
+        pairs = float(np.mean([pairs_q[j] for j in used_queries]))
+        alg_bytes = float(np.mean([bytes_q[j] for j in used_queries]))
+    else:
+        pairs = attended_pairs(layer, wl)
     flops_step = 4.0 * wl.head_dim * pairs
     value = flops_step / (ms_step * 1e-3) / 1e12
     rows = wl.n_q_heads * ((wl.n_tokens if wl.video_queries else 0) + n_extra)
     attn_ms = k_ms["attention"]
     if decode:
-        alg_bytes = decode_unique_bytes(layer, wl)
         achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_entry(wl.name),
@@ -634,18 +810,43 @@ def main():
                 "algorithmic_flops_per_launch": flops_step}
     roof["kernels"] = attention_kernels(wl, n_extra)
     roof["launch_ms"] = attn_ms  # one adas_sparse_attn_fwd call: the kernels above
-    stages = stage_rates(wl, n_extra, st_ms, roof)
+    stages = stage_rates(wl, n_extra, st_ms, roof, probes)
+    if decode:
+        step_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+        stages["decode_step"] = {"ms": ms_step, "bytes": alg_bytes, "bound": "hbm", "GB/s": step_gbs,
+                                 "frac": step_gbs / PEAK_HBM_GBS,
+                                 "frac_of_measured": (step_gbs / probes["hbm_read_GB/s"]) if probes else None,
+                                 "caches_flushed": flush is not None}
 
+    sel_stats = selection_stats(layer, wl)
     cpu = None
+    check = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, data, args.cpu_seconds, args.topk)
-
-    dens = None
-    if wl.video_queries:
-        cnt = layer.sel_count[:, : wl.n_tokens].to(torch.float64)
-        cubes = torch.arange(wl.n_tokens, device=dev) // wl.cube_size
-        cand = cubes.to(torch.float64).clamp_min(1)
-        dens = float((cnt / cand)[:, wl.cube_size:].mean().item())
+        sample = []
+        cpu = cpu_baseline(wl.replace(n_decode=n_queries) if decode else wl, data, args.cpu_seconds,
+                           args.topk, sample)
+        if decode:
+            # the sampled rows come from every decode query: select with each
+            # query block that holds some and grade those rows
+            B = args.decode_batch
+            check = None
+            for b in sorted({i_ // B for (_, _, i_, _, _) in sample}):
+                if b >= len(qe_steps):
+                    continue
+                layer.select(qe_steps[b])
+                torch.cuda.synchronize()
+                part = grade_sample(layer, wl, [(k_, hq, i_ - b * B, q_, kb_) for (k_, hq, i_, q_, kb_)
+                                                in sample if i_ // B == b], args.topk)
+                if check is None:
+                    check = part
+                else:
+                    check["rows"] += part["rows"]
+                    check["oracle_rows_within_1e-5_of_p"] += part["oracle_rows_within_1e-5_of_p"]
+                    for key in check["grades"]:
+                        check["grades"][key] += part["grades"][key]
+        else:
+            check = grade_sample(layer, wl, sample, args.topk)
+    dens = sel_stats.get("video_mean_selected_fraction", sel_stats["mean_selected_fraction"])
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -659,11 +860,19 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms": k_ms,
         "stages": stages,
+        "measured_peaks": probes,
         "queries_per_s": rows / (ms_step * 1e-3),
         "attended_pairs": pairs,
         "mean_selected_fraction": dens,
+        "selection": sel_stats,
+        "selection_check": check,
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
     }
+    if decode:
+        out["wall_ms_per_step"] = wall_ms_step
+        out["decode_protocol"] = (f"{len(qe_steps)} distinct query tokens in rotation; "
+                                  + ("512 MiB written between steps (outside the step's events)"
+                                     if flush is not None else "no cache flush"))
     print(json.dumps(out), flush=True)
 
 

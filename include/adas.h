@@ -305,6 +305,29 @@ const char* adas_last_error(void);
 /* "major.minor" */
 const char* adas_version(void);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not part of the method).  Peak probes give the ceiling
+ * the hardware sustains in isolation, so every stage of the path can be
+ * reported against a measured peak as well as the published one.  They are
+ * asynchronous on `stream` like the compute calls; the caller times them.
+ *
+ * adas_probe_mfma: `workgroups` workgroups of 4 waves, each wave running
+ *   `iters` loop trips of 16 v_mfma_f32_32x32x16_bf16 (4 independent chains)
+ *   on register operands.  *flops (host pointer, may be NULL) receives the
+ *   dense bf16 FLOPs issued.  sink: device float[workgroups], never written
+ *   in practice (it keeps the loop alive).  ADAS_ERR_VALUE for workgroups or
+ *   iters < 1.
+ * adas_probe_hbm_read: streams `bytes` (a positive multiple of 16) of src
+ *   once with 16-byte loads; sink: device uint32[workgroups] (never written in
+ *   practice).  workgroups < 1 means 8 per compute unit.
+ * adas_probe_hbm_copy: copies `bytes` (a positive multiple of 16) from src to
+ *   dst with 16-byte loads and stores.
+ * ------------------------------------------------------------------------- */
+adas_status adas_probe_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
+adas_status adas_probe_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                                void* stream);
+adas_status adas_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

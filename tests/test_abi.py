@@ -33,6 +33,20 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(L.EXPORTS)
 
 
+def test_probes_reject_invalid_arguments_on_host():
+    import ctypes
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    fl = ctypes.c_double(0.0)
+    assert lib.adas_probe_mfma(0, 10, ctypes.c_void_p(16), ctypes.byref(fl), None) == L.ADAS_ERR_VALUE
+    assert lib.adas_probe_mfma(8, 0, ctypes.c_void_p(16), ctypes.byref(fl), None) == L.ADAS_ERR_VALUE
+    assert lib.adas_probe_mfma(8, 10, None, ctypes.byref(fl), None) == L.ADAS_ERR_NULL
+    assert lib.adas_probe_hbm_read(None, 1024, ctypes.c_void_p(16), 0, None) == L.ADAS_ERR_NULL
+    assert lib.adas_probe_hbm_read(ctypes.c_void_p(16), 1000, ctypes.c_void_p(16), 0, None) == L.ADAS_ERR_SHAPE
+    assert lib.adas_probe_hbm_copy(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 0, None) == L.ADAS_ERR_SHAPE
+    assert lib.adas_probe_hbm_copy(ctypes.c_void_p(16), None, 1024, 0, None) == L.ADAS_ERR_NULL
+
+
 def _geom(**kw):
     import adaptive_cube_sparse_amd._lib as L
     base = dict(T=8, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=6, n_kv_heads=2, head_dim=128)
