@@ -31,7 +31,7 @@ SMALL = workloads.Workload(name="ties", T=8, H=16, W=16, ct=4, ch=4, cw=4, n_q_h
                            n_kv_heads=2, head_dim=128, dtype="bf16", p=P_TIE, seed=51)
 # few extra rows over 2048 cubes: the split selection path (one workgroup per row)
 SPLIT = workloads.Workload(name="ties_split", T=512, H=16, W=16, ct=4, ch=4, cw=4,
-                           n_q_heads=5, n_kv_heads=2, head_dim=128, dtype="bf16", p=P_TIE,
+                           n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16", p=P_TIE,
                            seed=52, video_queries=False, n_decode=3)
 # extra rows over 320 cubes next to video rows: the band kernels' extra-row tiles
 BANDS = workloads.Workload(name="ties_bands", T=20, H=16, W=16, ct=1, ch=4, cw=4,
