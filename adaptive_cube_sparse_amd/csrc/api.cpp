@@ -263,6 +263,7 @@ static adas_status attn_fwd(const adas_geom* geom, adas_dtype dtype, const void*
                     "adas_sparse_attn_fwd launch");
 }
 
+
 adas_status adas_sparse_attn_fwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
                                  const void* k_cube, const void* v_cube, int32_t n_extra,
                                  int32_t n_text_kv, const void* q_extra, const void* k_text,
@@ -391,7 +392,15 @@ size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kin
   adas::AttnArgs a;
   const int dummy = 1;
   if (build_attn(geom, dtype, has_video ? &dummy : nullptr, n_extra, 0, a) != ADAS_OK) return 0;
-  return adas::attention_workspace_bytes(a, dtype);
+  size_t bytes = adas::attention_workspace_bytes(a, dtype);
+  // the query does not know whether the extra rows will bring causal text
+  // keys, and without video rows that changes the plan (text keys rule out
+  // the decode kernel): size for the larger of the two plans
+  if (!has_video && n_extra > 0 && build_attn(geom, dtype, nullptr, n_extra, n_extra, a) == ADAS_OK) {
+    const size_t b2 = adas::attention_workspace_bytes(a, dtype);
+    if (b2 > bytes) bytes = b2;
+  }
+  return bytes;
 }
 
 int64_t adas_sel_capacity(const adas_geom* geom, int32_t has_video, int32_t n_extra) {
