@@ -29,7 +29,7 @@ from ._lib import (  # noqa: F401
     adas_ffn_fwd, adas_ffn_select, adas_ffn_workspace_bytes, adas_cache_append, adas_cache_sum_bytes,
     adas_sparse_attn_fwd_lse, adas_sparse_attn_bwd, ADAS_WS_BWD,
     adas_cube_mean_keys, adas_cube_partition, adas_select_topk, adas_select_topp, adas_sel_capacity,
-    adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load,
+    adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load, adas_sparse_attn_fwd_noalloc,
 )
 
 __all__ = [
@@ -39,7 +39,7 @@ __all__ = [
     "adas_version", "load", "LIB_PATH",
     "FfnGeometry", "AdasFFN", "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "StreamingCache",
-    "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd", "AdasAttentionGrad",
+    "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd", "AdasAttentionGrad", "adas_sparse_attn_fwd_noalloc",
 ]
 
 

@@ -25,6 +25,7 @@ ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT = 0, 1
 ADAS_MAX_HEADS = 128
 ADAS_MAX_CUBES = 4096
 ADAS_FFN_MAX_S = 256
+ADAS_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "adas_cube_partition", "adas_cube_mean_keys", "adas_select_topp", "adas_select_topk",
@@ -32,7 +33,7 @@ EXPORTS = (
     "adas_status_string", "adas_last_error", "adas_version",
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd",
-    "adas_probe_mfma", "adas_probe_hbm_read", "adas_probe_hbm_copy",
+    "adas_probe_mfma", "adas_probe_hbm_read", "adas_probe_hbm_copy", "adas_sparse_attn_fwd_noalloc",
 )
 
 
@@ -89,6 +90,8 @@ def load() -> ctypes.CDLL:
                                            vp, vp, vp, sz, vp]),
         "adas_sparse_attn_bwd": (i32, [gp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]),
+        "adas_sparse_attn_fwd_noalloc": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                               vp, vp]),
         "adas_probe_mfma": (i32, [i32, i32, vp, ctypes.POINTER(f64), vp]),
         "adas_probe_hbm_read": (i32, [vp, i64, vp, i32, vp]),
         "adas_probe_hbm_copy": (i32, [vp, vp, i64, i32, vp]),
@@ -265,7 +268,27 @@ def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text
                          ws: Optional[torch.Tensor] = None, stream=None) -> None:
     """Attention over selected cubes plus own cube (video rows) or selected
     cubes plus causal text (extra rows); see adas.h."""
-    lib = load()
+    args = _attn_args(geom, q_cube, k_cube, v_cube, q_extra, k_text, v_text, sel_count, sel_idx,
+                      out_raster, out_extra)
+    st = load().adas_sparse_attn_fwd(*args, _ptr(ws, name="ws"),
+                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "adas_sparse_attn_fwd")
+
+
+def adas_sparse_attn_fwd_noalloc(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text, v_text,
+                                 sel_count, sel_idx, out_raster, out_extra, stream=None) -> None:
+    """adas_sparse_attn_fwd without a workspace: the library's per-GPU scratch
+    array (ADAS_NOALLOC_SCRATCH_BYTES) takes its place; see adas.h."""
+    args = _attn_args(geom, q_cube, k_cube, v_cube, q_extra, k_text, v_text, sel_count, sel_idx,
+                      out_raster, out_extra)
+    st = load().adas_sparse_attn_fwd_noalloc(*args, _stream(stream))
+    _check(st, "adas_sparse_attn_fwd_noalloc")
+
+
+def _attn_args(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text, v_text, sel_count, sel_idx,
+               out_raster, out_extra):
+    """Shape checks and the pointer arguments shared by the attention calls
+    (geometry through out_extra)."""
     ref = q_cube if q_cube is not None else q_extra
     n_extra = 0 if q_extra is None else q_extra.shape[0]
     n_text_kv = 0 if k_text is None else k_text.shape[0]
@@ -281,15 +304,12 @@ def adas_sparse_attn_fwd(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text
         _shape(k_text, (n_text_kv, Hkv, d), "k_text")
         _shape(v_text, (n_text_kv, Hkv, d), "v_text")
     dt = ref.dtype
-    g, keep = geom._c()
-    st = lib.adas_sparse_attn_fwd(
-        ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, dt, "q_cube"), _ptr(k_cube, dt, "k_cube"),
-        _ptr(v_cube, dt, "v_cube"), n_extra, n_text_kv, _ptr(q_extra, dt, "q_extra"),
-        _ptr(k_text, dt, "k_text"), _ptr(v_text, dt, "v_text"),
-        _ptr(sel_count, torch.int32, "sel_count"), _ptr(sel_idx, torch.int32, "sel_idx"),
-        _ptr(out_raster, dt, "out_raster"), _ptr(out_extra, dt, "out_extra"),
-        _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "adas_sparse_attn_fwd")
+    g, keep = geom._c()   # byref(g) keeps g (and through it the head map) alive
+    return (ctypes.byref(g), _dtype_code(ref), _ptr(q_cube, dt, "q_cube"), _ptr(k_cube, dt, "k_cube"),
+            _ptr(v_cube, dt, "v_cube"), n_extra, n_text_kv, _ptr(q_extra, dt, "q_extra"),
+            _ptr(k_text, dt, "k_text"), _ptr(v_text, dt, "v_text"),
+            _ptr(sel_count, torch.int32, "sel_count"), _ptr(sel_idx, torch.int32, "sel_idx"),
+            _ptr(out_raster, dt, "out_raster"), _ptr(out_extra, dt, "out_extra"))
 
 
 def adas_cache_append(geom: Geometry, t0: int, k_new: torch.Tensor, v_new: torch.Tensor,

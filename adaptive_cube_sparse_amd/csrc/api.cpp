@@ -540,3 +540,17 @@ adas_status adas_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32
 }
 
 }  // extern "C"
+
+namespace adas {
+// Exact attention workspace of one call (0 when none is needed), for the
+// allocation-free entry point; validates like the call itself.
+adas_status attn_workspace_need(const adas_geom* geom, adas_dtype dtype, const void* q_cube, int32_t n_extra,
+                                int32_t n_text_kv, size_t* need) {
+  AttnArgs a;
+  adas_status st = build_attn(geom, dtype, q_cube, n_extra, n_text_kv, a);
+  if (st != ADAS_OK) return st;
+  *need = attention_workspace_bytes(a, dtype);
+  return ADAS_OK;
+}
+adas_status set_error(adas_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace adas

@@ -306,6 +306,35 @@ const char* adas_last_error(void);
 const char* adas_version(void);
 
 /* ---------------------------------------------------------------------------
+ * adas_sparse_attn_fwd_noalloc: adas_sparse_attn_fwd without a workspace
+ * argument, for callers that cannot allocate device memory (work recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, layouts, results and errors are those of
+ * adas_sparse_attn_fwd; the call allocates nothing.
+ *
+ * Its scratch (extra-row selection bitmaps and per-chunk partial rows, the
+ * memory adas_workspace_bytes(ADAS_WS_ATTN, ...) sizes) is a device array of
+ * ADAS_NOALLOC_SCRATCH_BYTES (16 MiB) that each GPU holds from the library's
+ * first use on it until the process ends.  A call whose scratch would exceed
+ * that returns ADAS_ERR_WORKSPACE and launches nothing; calls that need no
+ * scratch (video rows only) never touch it.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race on it and give undefined
+ * results.  Calls on one stream are ordered and safe.  The array needs no
+ * clearing between calls: each call writes all of the scratch it reads.
+ * The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) with that device current; a failure there returns
+ * ADAS_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+#define ADAS_NOALLOC_SCRATCH_BYTES (16u << 20)
+adas_status adas_sparse_attn_fwd_noalloc(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
+                                         const void* k_cube, const void* v_cube, int32_t n_extra,
+                                         int32_t n_text_kv, const void* q_extra, const void* k_text,
+                                         const void* v_text, const int32_t* sel_count,
+                                         const int32_t* sel_idx, void* out_raster, void* out_extra,
+                                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement helpers (not part of the method).  Peak probes give the ceiling
  * the hardware sustains in isolation, so every stage of the path can be
  * reported against a measured peak as well as the published one.  They are

@@ -234,3 +234,25 @@ def test_cache_geometry_and_append_validation():
     assert app(0, 4, L.ADAS_F32) == L.ADAS_ERR_DTYPE
     assert lib.adas_cache_append(ctypes.byref(g), L.ADAS_BF16, 0, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  None) == L.ADAS_ERR_NULL
+
+
+def test_noalloc_rejects_oversized_scratch_on_host():
+    """A call whose attention scratch exceeds ADAS_NOALLOC_SCRATCH_BYTES is
+    refused before anything is launched (pointers are never dereferenced on
+    the host): 64 decode rows x 28 heads over 4096 cubes need about 68 MB of
+    chunk partials."""
+    import ctypes
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _geom(T=1024, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=28, n_kv_heads=4, head_dim=128)
+    need = lib.adas_workspace_bytes(ctypes.byref(g), L.ADAS_BF16, L.ADAS_WS_ATTN, 0, 64)
+    assert need > L.ADAS_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(256)
+    st = lib.adas_sparse_attn_fwd_noalloc(ctypes.byref(g), L.ADAS_BF16, None, p, p, 64, 0, p, None, None,
+                                          p, p, None, p, None)
+    assert st == L.ADAS_ERR_WORKSPACE
+    assert b"allocation-free" in lib.adas_last_error()
+    # invalid geometry is reported as by adas_sparse_attn_fwd
+    g.head_dim = 96
+    assert lib.adas_sparse_attn_fwd_noalloc(ctypes.byref(g), L.ADAS_BF16, None, p, p, 1, 0, p, None, None,
+                                            p, p, None, p, None) == L.ADAS_ERR_SHAPE
