@@ -28,12 +28,14 @@ from ._lib import (  # noqa: F401
     AdasError, FfnGeometry, Geometry, LIB_PATH,
     adas_ffn_fwd, adas_ffn_select, adas_ffn_workspace_bytes, adas_cache_append, adas_cache_sum_bytes,
     adas_sparse_attn_fwd_lse, adas_sparse_attn_bwd, ADAS_WS_BWD,
-    adas_cube_mean_keys, adas_cube_partition, adas_select_topk, adas_select_topp, adas_sel_capacity,
+    adas_cube_mean_keys, adas_cube_partition, adas_cube_partition_keys, adas_select_topk, adas_select_topp,
+    adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load, adas_sparse_attn_fwd_noalloc,
 )
 
 __all__ = [
     "Geometry", "AdasAttention", "AdasError", "adas_cube_partition", "adas_cube_mean_keys",
+    "adas_cube_partition_keys",
     "adas_select_topp", "adas_select_topk", "adas_sparse_attn_fwd", "adas_workspace_bytes",
     "adas_sel_capacity",
     "adas_version", "load", "LIB_PATH",
@@ -82,12 +84,11 @@ class AdasAttention:
 
     # -- steps ---------------------------------------------------------------
     def build_kv(self, k_raster: torch.Tensor, v_raster: torch.Tensor, stream=None):
-        """Partition K (token rows) and V (cube-transposed) into cube layout and
-        compute the cube mean keys."""
+        """Partition K (token rows, with the cube mean keys in the same pass)
+        and V (cube-transposed) into cube layout."""
         g = self.geom
-        adas_cube_partition(g, k_raster, self.k_cube, self.perm, stream)
+        adas_cube_partition_keys(g, k_raster, self.k_cube, self.perm, self.kbar, stream)
         adas_cube_partition(g, v_raster, self.v_cube, None, stream, layout=ADAS_LAYOUT_VT)
-        adas_cube_mean_keys(g, self.k_cube, self.kbar, stream)
 
     def partition_queries(self, q_raster: torch.Tensor, stream=None):
         adas_cube_partition(self.geom, q_raster, self.q_cube, None, stream)

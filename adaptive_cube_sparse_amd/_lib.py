@@ -34,6 +34,7 @@ EXPORTS = (
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd",
     "adas_probe_mfma", "adas_probe_hbm_read", "adas_probe_hbm_copy", "adas_sparse_attn_fwd_noalloc",
+    "adas_cube_partition_keys",
 )
 
 
@@ -72,6 +73,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "adas_cube_partition": (i32, [gp, i32, i32, i32, vp, vp, vp, vp]),
         "adas_cube_mean_keys": (i32, [gp, i32, vp, vp, vp]),
+        "adas_cube_partition_keys": (i32, [gp, i32, vp, vp, vp, vp, vp]),
         "adas_select_topp": (i32, [gp, i32, vp, i32, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
         "adas_select_topk": (i32, [gp, i32, vp, i32, vp, vp, i32, vp, vp, i64, vp, sz, vp]),
         "adas_sparse_attn_fwd": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -224,6 +226,22 @@ def adas_cube_mean_keys(geom: Geometry, k_cube: torch.Tensor, kbar: torch.Tensor
     st = lib.adas_cube_mean_keys(ctypes.byref(g), _dtype_code(k_cube), _ptr(k_cube, name="k_cube"),
                                  _ptr(kbar, torch.float32, "kbar"), _stream(stream))
     _check(st, "adas_cube_mean_keys")
+
+
+def adas_cube_partition_keys(geom: Geometry, k_raster: torch.Tensor, k_cube: torch.Tensor,
+                             perm: Optional[torch.Tensor], kbar: torch.Tensor, stream=None) -> None:
+    """k_raster [N][Hkv][d] -> k_cube [Hkv][N][d], perm [N] int32 and kbar
+    [Hkv][Nc][d] float32 in one pass over K."""
+    lib = load()
+    _shape(k_raster, (geom.N, geom.n_kv_heads, geom.head_dim), "k_raster")
+    _shape(k_cube, (geom.n_kv_heads, geom.NS, geom.head_dim), "k_cube")
+    _shape(perm, (geom.N,), "perm")
+    _shape(kbar, (geom.n_kv_heads, geom.NS // geom.S, geom.head_dim), "kbar")
+    g, keep = geom._c()
+    st = lib.adas_cube_partition_keys(ctypes.byref(g), _dtype_code(k_raster), _ptr(k_raster, name="k_raster"),
+                                      _ptr(k_cube, k_raster.dtype, "k_cube"), _ptr(perm, torch.int32, "perm"),
+                                      _ptr(kbar, torch.float32, "kbar"), _stream(stream))
+    _check(st, "adas_cube_partition_keys")
 
 
 def _select(fn, name, geom, q_cube, q_extra, kbar, arg, sel_count, sel_idx, ws, stream):

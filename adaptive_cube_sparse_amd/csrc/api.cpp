@@ -143,6 +143,19 @@ adas_status adas_cube_mean_keys(const adas_geom* geom, adas_dtype dtype, const v
                     "adas_cube_mean_keys launch");
 }
 
+adas_status adas_cube_partition_keys(const adas_geom* geom, adas_dtype dtype, const void* k_raster,
+                                     void* k_cube, int32_t* perm, float* kbar, void* stream) {
+  adas::KGeom g;
+  adas::HeadGroups hg;
+  adas_status st = derive(geom, g, hg);
+  if (st != ADAS_OK) return st;
+  if ((st = check_dtype(dtype)) != ADAS_OK) return st;
+  if (k_raster == nullptr || k_cube == nullptr || kbar == nullptr)
+    return fail(ADAS_ERR_NULL, "k_raster/k_cube/kbar is NULL");
+  return hip_status(adas::launch_partition_keys(g, dtype, k_raster, k_cube, perm, kbar, (hipStream_t)stream),
+                    "adas_cube_partition_keys launch");
+}
+
 // Shared body of adas_select_topp / adas_select_topk (topk > 0 selects Top-K).
 static adas_status select_common(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
                                  int32_t n_extra, const void* q_extra, const float* kbar, float p,

@@ -357,6 +357,8 @@ hipError_t launch_partition(const KGeom& g, int elem_bytes, int nh, bool vt, con
                             void* dst, int32_t* perm, hipStream_t s);
 hipError_t launch_mean_keys(const KGeom& g, adas_dtype dt, const void* k, float* kbar,
                             hipStream_t s);
+hipError_t launch_partition_keys(const KGeom& g, adas_dtype dt, const void* src, void* dst, int32_t* perm,
+                                 float* kbar, hipStream_t s);
 hipError_t launch_cache_append(const KGeom& g, int f_lo, int f_hi, const void* k_new, const void* v_new,
                                void* k_cache, void* v_cache, float* kbar, double* ksum, hipStream_t s);
 

@@ -127,6 +127,95 @@ __global__ __launch_bounds__(256) void k_partition_vt(const T* __restrict__ src,
   }
 }
 
+// Keys: partition and mean keys in one pass, so K is read once.  One
+// workgroup per (cube, KV head) copies the cube's S rows as k_partition does;
+// with 256 threads and VPR 16-byte vectors per row (VPR divides 256), thread
+// t always copies vector t % VPR of rows t / VPR, t / VPR + 256 / VPR, ...,
+// and sums those EPV columns in float64.  The 256 / VPR threads of one vector
+// fold their sums with xor shuffles inside each wave, then across the four
+// waves through LDS.  The order of the additions differs from k_mean_keys';
+// the results agree bit for bit whenever the float64 sums are exact.
+template <typename T, int VPR>
+__global__ __launch_bounds__(256) void k_partition_keys(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        int32_t* __restrict__ perm, float* __restrict__ kbar,
+                                                        KGeom g) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int TPV = 256 / VPR;  // threads per vector column
+  static_assert(256 % VPR == 0 && VPR <= 64, "vectors per row");
+  __shared__ double part[4][VPR][EPV];
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int bx = c % g.nW;
+  const int by = (c / g.nW) % g.nH;
+  const int bt = c / (g.nW * g.nH);
+  const int hw = g.ch * g.cw;
+  const size_t dst_row0 = ((size_t)h * g.NS + (size_t)c * g.S);
+  const int v = threadIdx.x % VPR;
+  double acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+  for (int r = threadIdx.x / VPR; r < g.S; r += TPV) {
+    const int dt = r / hw;
+    const int rem = r - dt * hw;
+    const int dy = rem / g.cw;
+    const int dx = rem - dy * g.cw;
+    const int n = ((bt * g.ct + dt) * g.H + by * g.ch + dy) * g.W + bx * g.cw + dx;
+    const uint4 x = src[((size_t)n * g.Hkv + h) * VPR + v];
+    dst[(dst_row0 + r) * VPR + v] = x;
+    if (perm != nullptr && h == 0 && v == 0) perm[c * g.S + r] = n;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+        acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(w[e]);
+    }
+  }
+  // lanes v, v + VPR, ... of a wave hold the same column
+#pragma unroll
+  for (int o = VPR; o < kWave; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (lane < VPR) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) part[wave][lane][e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < VPR) {
+    float res[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const double sum = part[0][v][e] + part[1][v][e] + part[2][v][e] + part[3][v][e];
+      res[e] = (float)(sum / (double)g.S);
+    }
+    float* out = kbar + ((size_t)h * (g.NS / g.S) + c) * g.D + v * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4)
+      *reinterpret_cast<float4*>(out + e) = make_float4(res[e], res[e + 1], res[e + 2], res[e + 3]);
+  }
+}
+
+hipError_t launch_partition_keys(const KGeom& g, adas_dtype dt, const void* src, void* dst, int32_t* perm,
+                                 float* kbar, hipStream_t s) {
+  const dim3 grid(g.Nc, g.Hkv);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, kbar, g);
+  };
+  if (dt == ADAS_BF16) {
+    if (g.D == 128) go(k_partition_keys<uint16_t, 16>);
+    else go(k_partition_keys<uint16_t, 8>);
+  } else {
+    if (g.D == 128) go(k_partition_keys<float, 32>);
+    else go(k_partition_keys<float, 16>);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_partition_frames(const KGeom& g, int elem_bytes, int nh, bool vt, const void* src,
                                    void* dst, int32_t* perm, int f_lo, int f_hi, hipStream_t s) {
   const int per_block = g.nH * g.nW;

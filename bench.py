@@ -215,12 +215,12 @@ def decode_unique_bytes(layer, wl) -> int:
 
 def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict, probes=None) -> dict:
     """Each step of the path against the MI355X peak that bounds it: the
-    cube gather (partition of Q, K, V: every element read and written once,
-    plus perm) and the mean-key reduction (K read, float32 mean keys written)
-    against HBM; the selection's scoring product (2 d flops per candidate of
-    every row) against the bf16 MFMA peak; the attention call as in the
-    roofline.  For decode workloads the gather and reduction are those of the
-    cache build, timed once before the steps."""
+    key pass (K partitioned, read and written once, plus perm and the float32
+    mean keys) and the gather of V and Q (read and written once) against
+    HBM; the selection's scoring product (2 d flops per candidate of every
+    row) against the bf16 MFMA peak; the attention call as in the roofline.
+    For decode workloads the key pass and gather are those of the cache
+    build, timed once before the steps."""
     el = 2 if wl.dtype == "bf16" else 4
     d, N, Hq, Hkv = wl.head_dim, wl.n_tokens, wl.n_q_heads, wl.n_kv_heads
     S = wl.cube_size
@@ -228,16 +228,16 @@ def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict, probes=None) -> dict:
     q_el = N * Hq * d if wl.video_queries else 0
     kv_el = N * Hkv * d
     out = {}
+    if "keys" in st_ms:
+        b = 2 * el * kv_el + 4 * N + 4 * Hkv * Nc * d
+        out["keys"] = {"ms": st_ms["keys"], "bytes": b, "bound": "hbm",
+                       "GB/s": b / (st_ms["keys"] * 1e-3) / 1e9,
+                       "frac": b / (st_ms["keys"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if "gather" in st_ms:
-        b = 2 * el * (q_el + 2 * kv_el) + 4 * N
+        b = 2 * el * (q_el + kv_el)
         out["gather"] = {"ms": st_ms["gather"], "bytes": b, "bound": "hbm",
                          "GB/s": b / (st_ms["gather"] * 1e-3) / 1e9,
                          "frac": b / (st_ms["gather"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    if "mean_keys" in st_ms:
-        b = el * kv_el + 4 * Hkv * Nc * d
-        out["mean_keys"] = {"ms": st_ms["mean_keys"], "bytes": b, "bound": "hbm",
-                            "GB/s": b / (st_ms["mean_keys"] * 1e-3) / 1e9,
-                            "frac": b / (st_ms["mean_keys"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
     cand = (Hq * S * Nc * (Nc - 1) // 2 if wl.video_queries else 0) + Hq * n_extra * Nc
     f = 2.0 * d * cand
     t = f / (st_ms["select"] * 1e-3) / 1e12
@@ -247,10 +247,9 @@ def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict, probes=None) -> dict:
     out["attention"] = {"ms": roof["launch_ms"], "bound": roof["bound"], "achieved": roof["achieved"],
                         "unit": roof["unit"], "frac": roof["frac"]}
     if probes:
-        for k in ("gather", "mean_keys"):
+        for k in ("keys", "gather"):
             if k in out:
-                out[k]["frac_of_measured"] = out[k]["GB/s"] / probes["hbm_copy_GB/s" if k == "gather" else
-                                                                       "hbm_read_GB/s"]
+                out[k]["frac_of_measured"] = out[k]["GB/s"] / probes["hbm_copy_GB/s"]
         out["select"]["scoring_frac_of_measured"] = t / probes["mfma_bf16_TFLOP/s"]
         ref = probes["mfma_bf16_TFLOP/s"] if roof["unit"] == "TFLOP/s" else probes["hbm_read_GB/s"]
         out["attention"]["frac_of_measured"] = roof["achieved"] / ref
@@ -698,14 +697,17 @@ def main():
         qe_steps = [qe_all[(i % nb) * args.decode_batch:(i % nb + 1) * args.decode_batch].contiguous()
                     for i in range(nb)]
         qe = qe_steps[0]
-    flush = None
+    flush = flush_sink = None
     if decode and not args.no_flush:
-        # 512 MiB written between decode steps evicts L2 and the memory-side cache
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # 512 MiB read between decode steps evicts L2 and the memory-side
+        # cache (256 MB) and leaves them clean: a written flush would leave
+        # dirty lines whose write-back lands inside the timed step
+        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+        flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
     kt = up(data["k_text"]) if n_text_kv else None
     vt = up(data["v_text"]) if n_text_kv else None
     stream = torch.cuda.current_stream()
-    from adaptive_cube_sparse_amd import ADAS_LAYOUT_VT, adas_cube_mean_keys, adas_cube_partition
+    from adaptive_cube_sparse_amd import ADAS_LAYOUT_VT, adas_cube_partition, adas_cube_partition_keys
 
     def mark():
         e = torch.cuda.Event(enable_timing=True)
@@ -713,28 +715,26 @@ def main():
         return e
 
     def layout(record):
-        """Partition K, V (and Q), then the mean keys: the calls of
-        AdasAttention.build_kv / partition_queries, with an event between the
-        gather and the reduction."""
+        """The key pass (K partition + mean keys), then V (and Q): the calls of
+        AdasAttention.build_kv / partition_queries, with an event between."""
         g = layer.geom
         e0 = mark() if record else None
-        adas_cube_partition(g, k, layer.k_cube, layer.perm)
+        adas_cube_partition_keys(g, k, layer.k_cube, layer.perm, layer.kbar)
+        e1 = mark() if record else None
         adas_cube_partition(g, v, layer.v_cube, None, layout=ADAS_LAYOUT_VT)
         if q is not None:
             adas_cube_partition(g, q, layer.q_cube, None)
-        e1 = mark() if record else None
-        adas_cube_mean_keys(g, layer.k_cube, layer.kbar)
         e2 = mark() if record else None
         return e0, e1, e2
 
-    ev = {name: [] for name in ("layout", "gather", "mean_keys", "select", "attention")}
+    ev = {name: [] for name in ("layout", "keys", "gather", "select", "attention")}
     if decode:
         # the cache exists before decoding starts; its build is timed once here
         for _ in range(2):
             lay = layout(True)
         torch.cuda.synchronize()
-        ev["gather"].append((lay[0], lay[1]))
-        ev["mean_keys"].append((lay[1], lay[2]))
+        ev["keys"].append((lay[0], lay[1]))
+        ev["gather"].append((lay[1], lay[2]))
 
     used_queries = []
 
@@ -748,7 +748,7 @@ def main():
             if record:
                 used_queries.append(i % len(qe_steps))
             if flush is not None:
-                flush.zero_()
+                torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink)
             e2 = mark() if record else None
         layer.select(q_i)
         e3 = mark() if record else None
@@ -757,8 +757,8 @@ def main():
         if record:
             if not decode:
                 ev["layout"].append((e0, e2))  # partition Q/K/V + mean keys
-                ev["gather"].append((e0, e1))
-                ev["mean_keys"].append((e1, e2))
+                ev["keys"].append((e0, e1))
+                ev["gather"].append((e1, e2))
             ev["select"].append((e2, e3))
             ev["attention"].append((e3, e4))
 
@@ -871,7 +871,7 @@ def main():
     if decode:
         out["wall_ms_per_step"] = wall_ms_step
         out["decode_protocol"] = (f"{len(qe_steps)} distinct query tokens in rotation; "
-                                  + ("512 MiB written between steps (outside the step's events)"
+                                  + ("512 MiB read between steps (outside the step's events)"
                                      if flush is not None else "no cache flush"))
     print(json.dumps(out), flush=True)
 

@@ -127,6 +127,25 @@ adas_status adas_cube_mean_keys(const adas_geom* geom, adas_dtype dtype, const v
                                 float* kbar, void* stream);
 
 /*
+ * adas_cube_partition_keys -- adas_cube_partition of the keys
+ * (ADAS_LAYOUT_TOKENS, n_heads = n_kv_heads) and adas_cube_mean_keys in one
+ * pass, so K is read from memory once (papernotes.org, key designs 1 and 2).
+ *   k_raster [N][Hkv][d]  keys, raster token order
+ *   k_cube   [Hkv][N][d]  output, as adas_cube_partition
+ *   perm     [N] int32    output (nullable), as adas_cube_partition
+ *   kbar     [Hkv][Nc][d] float32 output, as adas_cube_mean_keys: float64
+ *                        sums, rounded once.  The rows are added in another
+ *                        order than adas_cube_mean_keys adds them, so the two
+ *                        agree bit for bit whenever the float64 sums are
+ *                        exact; with S <= 256 that holds when a cube's
+ *                        nonzero key magnitudes lie within a factor 2^37
+ *                        (bf16) or 2^21 (float32) of each other.
+ * Errors: NULL, SHAPE, DTYPE, HIP.
+ */
+adas_status adas_cube_partition_keys(const adas_geom* geom, adas_dtype dtype, const void* k_raster,
+                                     void* k_cube, int32_t* perm, float* kbar, void* stream);
+
+/*
  * adas_select_topp -- selection softmax and Top-p cube sets (papernotes.org,
  * key design 2, the P_i and S_i equations; key design 4, one threshold p).
  *

@@ -159,6 +159,9 @@ def test_attention_and_partition_reject_invalid_arguments_on_host():
     assert lib.adas_cube_partition(ctypes.byref(g), L.ADAS_BF16, 2, 5, FAKE, FAKE, None, None) == L.ADAS_ERR_VALUE
     assert "layout" in lib.adas_last_error().decode()
     assert lib.adas_cube_mean_keys(ctypes.byref(g), L.ADAS_BF16, None, FAKE, None) == L.ADAS_ERR_NULL
+    assert lib.adas_cube_partition_keys(ctypes.byref(g), L.ADAS_BF16, FAKE, FAKE, None, None,
+                                        None) == L.ADAS_ERR_NULL
+    assert lib.adas_cube_partition_keys(ctypes.byref(g), 9, FAKE, FAKE, None, FAKE, None) == L.ADAS_ERR_DTYPE
 
     def attn(**kw):
         a = dict(q_cube=FAKE, k=FAKE, v=FAKE, n_extra=0, n_text_kv=0, q_extra=None, kt=None, vt=None,
