@@ -34,7 +34,7 @@ EXPORTS = (
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd",
     "adas_probe_mfma", "adas_probe_hbm_read", "adas_probe_hbm_copy", "adas_sparse_attn_fwd_noalloc",
-    "adas_cube_partition_keys",
+    "adas_cube_partition_keys", "adas_probe_attn_mix",
 )
 
 
@@ -97,6 +97,7 @@ def load() -> ctypes.CDLL:
         "adas_probe_mfma": (i32, [i32, i32, vp, ctypes.POINTER(f64), vp]),
         "adas_probe_hbm_read": (i32, [vp, i64, vp, i32, vp]),
         "adas_probe_hbm_copy": (i32, [vp, vp, i64, i32, vp]),
+        "adas_probe_attn_mix": (i32, [i32, i32, i32, vp, i64, vp, ctypes.POINTER(f64), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -455,6 +456,22 @@ def adas_probe_mfma(workgroups: int, iters: int, sink: torch.Tensor, stream=None
     st = lib.adas_probe_mfma(int(workgroups), int(iters), _ptr(sink, torch.float32, "sink"), ctypes.byref(fl),
                              _stream(stream))
     _check(st, "adas_probe_mfma")
+    return fl.value
+
+
+def adas_probe_attn_mix(workgroups: int, iters: int, mix: bool, src: Optional[torch.Tensor], sink: torch.Tensor,
+                        stream=None) -> float:
+    """Launch the MFMA loop alone (mix False) or with the union attention's
+    side work (mix True; src: a device buffer of at least 2 MiB); returns the
+    dense bf16 FLOPs it issues."""
+    lib = load()
+    _shape(sink, (workgroups,), "sink")
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    fl = ctypes.c_double(0.0)
+    st = lib.adas_probe_attn_mix(int(workgroups), int(iters), 1 if mix else 0,
+                                 None if src is None else _ptr(src, name="src"), nbytes,
+                                 _ptr(sink, torch.float32, "sink"), ctypes.byref(fl), _stream(stream))
+    _check(st, "adas_probe_attn_mix")
     return fl.value
 
 

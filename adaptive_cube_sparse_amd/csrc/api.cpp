@@ -552,6 +552,22 @@ adas_status adas_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32
                     "adas_probe_hbm_copy launch");
 }
 
+adas_status adas_probe_attn_mix(int32_t workgroups, int32_t iters, int32_t mix, const void* src, int64_t src_bytes,
+                                float* sink, double* flops, void* stream) {
+  if (workgroups < 1 || iters < 1) return fail(ADAS_ERR_VALUE, "workgroups and iters must be >= 1");
+  if (mix != 0 && mix != 1) return fail(ADAS_ERR_VALUE, "mix must be 0 or 1 (got %d)", mix);
+  if (sink == nullptr) return fail(ADAS_ERR_NULL, "sink is NULL");
+  if (mix == 1) {
+    if (src == nullptr) return fail(ADAS_ERR_NULL, "src is NULL");
+    if (src_bytes < (2 << 20) || src_bytes >= 0x80000000LL)
+      return fail(ADAS_ERR_SHAPE, "src_bytes must be in [2 MiB, 2 GiB)");
+  }
+  if (flops != nullptr) *flops = adas::probe_attn_mix_flops_per_wg(iters) * workgroups;
+  return hip_status(adas::launch_probe_attn_mix(workgroups, iters, mix == 1, src, (int)src_bytes, sink,
+                                                (hipStream_t)stream),
+                    "adas_probe_attn_mix launch");
+}
+
 }  // extern "C"
 
 namespace adas {

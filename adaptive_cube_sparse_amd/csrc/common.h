@@ -426,5 +426,8 @@ double probe_mfma_flops_per_wg(int iters);
 hipError_t launch_probe_mfma(int wgs, int iters, float* sink, hipStream_t s);
 hipError_t launch_probe_read(const void* src, long bytes, uint32_t* sink, int wgs, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, long bytes, int wgs, hipStream_t s);
+double probe_attn_mix_flops_per_wg(int iters);
+hipError_t launch_probe_attn_mix(int wgs, int iters, bool mix, const void* src, int src_bytes, float* sink,
+                                 hipStream_t s);
 
 }  // namespace adas

@@ -63,6 +63,98 @@ __global__ __launch_bounds__(256) void k_probe_copy(const pu32x4* __restrict__ s
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// The union attention's instruction mix around its MFMAs, without its data
+// flow: 8 waves (two per SIMD), each trip 32 v_mfma_f32_32x32x16_bf16 on four
+// accumulators with operands of realistic bit activity (bf16 in +-[0.5, 1)
+// with random mantissas and signs).  MIX adds, per MFMA, what one score or
+// output MFMA of a key block brings with it: one 16-byte LDS operand read, one
+// exp2 of an fma, and per two MFMAs a bf16 pack and a dot2 row-sum step; per
+// trip four 1 KB global->LDS loads per wave (a 32 KB block per workgroup, from
+// a 2 MB window of src that stays in L2); a barrier after every second trip,
+// after the loads have landed.  Without MIX the same loop runs the MFMAs alone.
+namespace {
+typedef __bf16 mbf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t mix_bits(uint32_t h) {
+  h ^= h >> 15;
+  h *= 0x2c1b3c6du;
+  h ^= h >> 12;
+  h *= 0x297a2d39u;
+  h ^= h >> 15;
+  return (h & 0x807F807Fu) | 0x3F003F00u;  // two bf16 in +-[0.5, 1)
+}
+}  // namespace
+
+template <bool MIX>
+__global__ __launch_bounds__(512) void k_probe_attn_mix(int iters, const void* src, int src_bytes, float* sink) {
+  __shared__ pu32x4 ops[4096];           // 64 KB of operands
+  __shared__ pu32x4 dst[2][8][4][64];    // load targets: two 32 KB blocks
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < 4096; i += 512)
+    ops[i] = (pu32x4){mix_bits(4 * i), mix_bits(4 * i + 1), mix_bits(4 * i + 2), mix_bits(4 * i + 3)};
+  __syncthreads();
+  const pu32x4 xa = {mix_bits(99991u * t + 1), mix_bits(99991u * t + 2), mix_bits(99991u * t + 3),
+                     mix_bits(99991u * t + 4)};
+  const pu32x4 xb = {mix_bits(77777u * t + 1), mix_bits(77777u * t + 2), mix_bits(77777u * t + 3),
+                     mix_bits(77777u * t + 4)};
+  const pbf16x8 b = __builtin_bit_cast(pbf16x8, xb);
+  const mbf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  pf32x16 acc[4];
+  pf32x16 sv;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[0][i] = acc[1][i] = acc[2][i] = acc[3][i] = 0.f;
+    sv[i] = 0.001f * (float)(i + lane);
+  }
+  float ls = 0.f;
+  const uint32_t window = (uint32_t)(blockIdx.x % 32) * 65536u;  // 64 KB per trip pair, 2 MB in all
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MIX) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        buffer_load_lds16((void*)src, src_bytes, &dst[it & 1][w][k][0],
+                          window + (uint32_t)((((it & 1) * 8 + w) * 4 + k) * 1024 + lane * 16), 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      pbf16x8 a;
+      if constexpr (MIX) a = __builtin_bit_cast(pbf16x8, ops[(r * 128 + w * 16 + lane + it * 64) & 4095]);
+      else a = __builtin_bit_cast(pbf16x8, xa);
+      acc[r & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[r & 3], 0, 0, 0);
+      if constexpr (MIX) {
+        const int e = r & 15;
+        sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], 0.5f, -0.25f));
+        if (r & 1) {
+          const mbf16x2 pr = {(__bf16)sv[e - 1], (__bf16)sv[e]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+        }
+      }
+    }
+    if constexpr (MIX) {
+      if (it & 1) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+      }
+    }
+  }
+  if constexpr (MIX) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  float s = ls + (MIX ? (float)dst[0][w][0][lane][0] : 0.f);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += acc[0][i] + acc[1][i] + acc[2][i] + acc[3][i] + sv[i];
+  if (s == 1234.5f) sink[blockIdx.x] = s;  // practically never; keeps the loop
+}
+
+double probe_attn_mix_flops_per_wg(int iters) { return 8.0 * iters * 32 * (2.0 * 32 * 32 * 16); }
+
+hipError_t launch_probe_attn_mix(int wgs, int iters, bool mix, const void* src, int src_bytes, float* sink,
+                                 hipStream_t s) {
+  if (mix)
+    hipLaunchKernelGGL(k_probe_attn_mix<true>, dim3((unsigned)wgs), dim3(512), 0, s, iters, src, src_bytes, sink);
+  else
+    hipLaunchKernelGGL(k_probe_attn_mix<false>, dim3((unsigned)wgs), dim3(512), 0, s, iters, src, src_bytes, sink);
+  return hipGetLastError();
+}
+
 double probe_mfma_flops_per_wg(int iters) {
   // 4 waves, each kProbeChains x kProbeUnroll MFMAs of 32x32x16 per trip
   return 4.0 * iters * kProbeChains * kProbeUnroll * (2.0 * 32 * 32 * 16);

@@ -257,11 +257,15 @@ def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict, probes=None) -> dict:
 
 
 def peak_probes() -> dict:
-    """Measured ceilings: an MFMA-only register loop (dense bf16) and
-    streaming HBM reads / copies of 2 GiB (far beyond the 256 MB of on-die
-    caches), each timed with HIP events, best of three."""
+    """Measured ceilings: an MFMA-only register loop (dense bf16), the same
+    MFMAs with the union attention's side work per MFMA (LDS operand read,
+    exp / pack / row-sum, global->LDS staging, barriers: the ceiling of that
+    kernel's instruction mix), and streaming HBM reads / copies of 2 GiB (far
+    beyond the 256 MB of on-die caches), each timed with HIP events, best of
+    three."""
     import torch
-    from adaptive_cube_sparse_amd._lib import adas_probe_hbm_copy, adas_probe_hbm_read, adas_probe_mfma
+    from adaptive_cube_sparse_amd._lib import (adas_probe_attn_mix, adas_probe_hbm_copy, adas_probe_hbm_read,
+                                               adas_probe_mfma)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
@@ -285,6 +289,15 @@ def peak_probes() -> dict:
         fl[0] = adas_probe_mfma(wgs, 2000, sink)
     t = best(mf)
     mfma = fl[0] / t / 1e12
+    mix_src = torch.zeros(4 << 20, dtype=torch.uint8, device=dev)
+    msink = torch.zeros(1024, dtype=torch.float32, device=dev)
+    mix_rate = {}
+    for mix in (False, True):
+        def mx():
+            fl[0] = adas_probe_attn_mix(1024, 1000, mix, mix_src, msink)
+        tm = best(mx)
+        mix_rate[mix] = fl[0] / tm / 1e12
+    del mix_src
     n = 2 << 30
     src = torch.ones(n // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
@@ -294,8 +307,10 @@ def peak_probes() -> dict:
     del src, dst
     torch.cuda.empty_cache()
     return {"mfma_bf16_TFLOP/s": mfma, "hbm_read_GB/s": n / t_r / 1e9, "hbm_copy_GB/s": 2 * n / t_c / 1e9,
-            "note": "MFMA-only register loop (2048 workgroups x 4 waves x 4 chains); 2 GiB streams; "
-                    "best of 3, HIP events"}
+            "mfma_random_operands_TFLOP/s": mix_rate[False], "attn_mix_ceiling_TFLOP/s": mix_rate[True],
+            "note": "MFMA-only register loop (2048 workgroups x 4 waves x 4 chains); the union attention's "
+                    "instruction mix around the same MFMAs and those MFMAs alone, random-mantissa bf16 operands "
+                    "(1024 workgroups x 8 waves); 2 GiB streams; best of 3, HIP events"}
 
 
 def selection_stats(layer, wl) -> dict:

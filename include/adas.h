@@ -370,11 +370,26 @@ adas_status adas_sparse_attn_fwd_noalloc(const adas_geom* geom, adas_dtype dtype
  *   practice).  workgroups < 1 means 8 per compute unit.
  * adas_probe_hbm_copy: copies `bytes` (a positive multiple of 16) from src to
  *   dst with 16-byte loads and stores.
+ * adas_probe_attn_mix: `workgroups` workgroups of 8 waves (two per SIMD, as in
+ *   the union attention), each wave running `iters` trips of 32
+ *   v_mfma_f32_32x32x16_bf16 on four accumulators, with bf16 operands of
+ *   random mantissas and signs.  mix = 0: the MFMAs alone.  mix = 1: with the
+ *   attention's side work per MFMA (a 16-byte LDS operand read, an exp2 of an
+ *   fma, half a bf16 pack and half a dot2 row-sum step), four 1 KB
+ *   global->LDS loads per wave and trip from a 2 MB window of src, and a
+ *   barrier every second trip.  src: device buffer of src_bytes >= 2 MiB
+ *   (read, contents irrelevant; needed for mix = 1, may be NULL for 0).
+ *   *flops (host, may be NULL) receives the FLOPs issued; sink: device
+ *   float[workgroups], never written in practice.  ADAS_ERR_VALUE for
+ *   workgroups or iters < 1 or mix not 0/1; ADAS_ERR_SHAPE for src_bytes below
+ *   2 MiB or at least 2^31 when mix = 1.
  * ------------------------------------------------------------------------- */
 adas_status adas_probe_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
 adas_status adas_probe_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
                                 void* stream);
 adas_status adas_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32_t workgroups, void* stream);
+adas_status adas_probe_attn_mix(int32_t workgroups, int32_t iters, int32_t mix, const void* src, int64_t src_bytes,
+                                float* sink, double* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,12 @@ def test_probes_reject_invalid_arguments_on_host():
     assert lib.adas_probe_hbm_read(ctypes.c_void_p(16), 1000, ctypes.c_void_p(16), 0, None) == L.ADAS_ERR_SHAPE
     assert lib.adas_probe_hbm_copy(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 0, None) == L.ADAS_ERR_SHAPE
     assert lib.adas_probe_hbm_copy(ctypes.c_void_p(16), None, 1024, 0, None) == L.ADAS_ERR_NULL
+    assert lib.adas_probe_attn_mix(0, 10, 0, None, 0, ctypes.c_void_p(16), ctypes.byref(fl), None) == L.ADAS_ERR_VALUE
+    assert lib.adas_probe_attn_mix(8, 10, 2, None, 0, ctypes.c_void_p(16), ctypes.byref(fl), None) == L.ADAS_ERR_VALUE
+    assert lib.adas_probe_attn_mix(8, 10, 1, None, 4 << 20, ctypes.c_void_p(16), ctypes.byref(fl),
+                                   None) == L.ADAS_ERR_NULL
+    assert lib.adas_probe_attn_mix(8, 10, 1, ctypes.c_void_p(16), 1 << 20, ctypes.c_void_p(16), ctypes.byref(fl),
+                                   None) == L.ADAS_ERR_SHAPE
 
 
 def _geom(**kw):
