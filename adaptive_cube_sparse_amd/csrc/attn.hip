@@ -91,9 +91,17 @@ __global__ __launch_bounds__(256) void k_extra_bitmap(AttnArgs a) {
   __syncthreads();
   const int cnt = a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? a.g.N : 0) + m];
   const int32_t* list = a.sel_idx + extra_list_offset(a.capv, a.g.Hq, a.n_extra, a.g.Nc, hq, m);
-  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
-    const int j = list[i];
-    atomicOr(&words[j >> 5], 1u << (j & 31));
+  // four list entries per thread in flight before the first LDS update
+  for (int i0 = threadIdx.x; i0 < cnt; i0 += 4 * blockDim.x) {
+    int j[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * blockDim.x;
+      j[u] = i < cnt ? list[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j[u] >= 0) atomicOr(&words[j[u] >> 5], 1u << (j[u] & 31));
   }
   __syncthreads();
   uint32_t* dst = a.extra_bits + (size_t)row * W;

@@ -256,6 +256,42 @@ def stage_rates(wl, n_extra: int, st_ms: dict, roof: dict, probes=None) -> dict:
     return out
 
 
+def decode_graph_ms(layer, qe_steps, used, flush, flush_sink, stream) -> float:
+    """Mean event-timed duration of one decode step (selection + attention)
+    replayed from a captured HIP graph: the step reads its query from a
+    static buffer that each step's token is copied into first, and the caches
+    are flushed before each replay, both outside the events."""
+    import torch
+    q_static = torch.empty_like(qe_steps[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q_static.copy_(qe_steps[0])
+        layer.select(q_static)
+        layer.attend(q_static, None, None)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.select(q_static)
+        layer.attend(q_static, None, None)
+    torch.cuda.synchronize()
+    pairs = []
+    for j in used:
+        q_static.copy_(qe_steps[j])
+        if flush is not None:
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    del graph
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
 def peak_probes() -> dict:
     """Measured ceilings: an MFMA-only register loop (dense bf16), the same
     MFMAs with the union attention's side work per MFMA (LDS operand read,
@@ -832,6 +868,14 @@ def main():
                                  "frac": step_gbs / PEAK_HBM_GBS,
                                  "frac_of_measured": (step_gbs / probes["hbm_read_GB/s"]) if probes else None,
                                  "caches_flushed": flush is not None}
+        if args.decode_batch == 1:
+            g_ms = decode_graph_ms(layer, qe_steps, used_queries, flush, flush_sink, stream)
+            g_gbs = alg_bytes / (g_ms * 1e-3) / 1e9
+            stages["decode_step_graph"] = {
+                "ms": g_ms, "GB/s": g_gbs, "frac": g_gbs / PEAK_HBM_GBS,
+                "frac_of_measured": (g_gbs / probes["hbm_read_GB/s"]) if probes else None,
+                "note": "the same steps (same query rotation and cache flush) with selection and attention "
+                        "replayed from one captured HIP graph; event-timed per replay"}
 
     sel_stats = selection_stats(layer, wl)
     cpu = None
