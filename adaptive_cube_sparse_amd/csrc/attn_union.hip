@@ -736,8 +736,18 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       my_lo = lo;
       const uint32_t bit = 1u << (my_row & 31);
       uint32_t* wbase = &s_bits[my_row >> 5];
-#pragma unroll 4
-      for (int i = lo + my_half; i < lo2; i += 2) atomicOr(wbase + UNW * (my_list[i] - jb), bit);
+      // eight list entries per thread in flight before their LDS updates
+      for (int i0 = lo + my_half; i0 < lo2; i0 += 16) {
+        int e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + 2 * u;
+          e[u] = i < lo2 ? my_list[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (e[u] >= 0) atomicOr(wbase + UNW * (e[u] - jb), bit);
+      }
       if (my_half == 0 && my_c >= jb && my_c < je) atomicOr(wbase + UNW * (my_c - jb), bit);
     }
     __syncthreads();
