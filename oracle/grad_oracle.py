@@ -62,14 +62,17 @@ def row_weights(q: np.ndarray, keys: np.ndarray, values: np.ndarray, do: np.ndar
 
 
 def attention_grads(q_cube, k_cube, v_cube, g: Geometry, sel_video: dict, dout_raster,
-                    q_extra=None, sel_extra=None, dout_extra=None, head_map=None):
+                    q_extra=None, sel_extra=None, dout_extra=None, head_map=None, k_text=None, v_text=None):
     """Gradients of every row in ``sel_video`` ({(hq, pos): cubes}) and
-    ``sel_extra`` ({(hq, m): cubes}; extra rows attend their selected cubes
-    only).  Cube-layout inputs as from ``partition``; dout_raster [N][Hq][d]
+    ``sel_extra`` ({(hq, m): cubes}; extra rows attend their selected cubes,
+    and, with ``k_text`` / ``v_text`` [n_text][Hkv][d] given, text keys 0..m
+    as well: a text prefill, where text row m attends the text tokens up to
+    itself).  Cube-layout inputs as from ``partition``; dout_raster [N][Hq][d]
     (raster order), dout_extra [n_extra][Hq][d].
 
     Returns dict with float64 arrays: dq_raster [N][Hq][d] (rows not listed
     are zero), dk_raster / dv_raster [N][Hkv][d], dq_extra [n_extra][Hq][d],
+    dk_text / dv_text [n_text][Hkv][d] (with text keys),
     lse {(kind, hq, row): value}, o {(kind, hq, row): [d]}."""
     Hq, N, d = q_cube.shape
     Hkv = k_cube.shape[0]
@@ -83,17 +86,28 @@ def attention_grads(q_cube, k_cube, v_cube, g: Geometry, sel_video: dict, dout_r
     dv = np.zeros((g.N, Hkv, d))
     n_extra = 0 if q_extra is None else q_extra.shape[0]
     dqx = np.zeros((n_extra, Hq, d))
+    n_text = 0 if k_text is None else k_text.shape[0]
+    dkt = np.zeros((n_text, Hkv, d))
+    dvt = np.zeros((n_text, Hkv, d))
     lse, outs = {}, {}
 
-    def run(kind, hq, row, qv, dov, cubes):
+    def run(kind, hq, row, qv, dov, cubes, n_tk=0):
+        """n_tk: text keys 0 .. n_tk - 1 join the row's keys after its cubes."""
         kv = _kv_head(hq, Hq, Hkv, head_map)
         pos = np.concatenate([np.arange(j * S, (j + 1) * S) for j in cubes]) if cubes else np.zeros(0, np.int64)
         keys = to_f64(k_cube[kv][pos])
         vals = to_f64(v_cube[kv][pos])
+        if n_tk:
+            keys = np.concatenate([keys, to_f64(k_text[:n_tk, kv])])
+            vals = np.concatenate([vals, to_f64(v_text[:n_tk, kv])])
         o, l, gq, gk, gv = attend_grad(qv, keys, vals, dov)
+        nv = len(pos)
         ras = raster_of_pos[pos]
-        np.add.at(dk[:, kv], ras, gk)
-        np.add.at(dv[:, kv], ras, gv)
+        np.add.at(dk[:, kv], ras, gk[:nv])
+        np.add.at(dv[:, kv], ras, gv[:nv])
+        if n_tk:
+            dkt[:n_tk, kv] += gk[nv:]
+            dvt[:n_tk, kv] += gv[nv:]
         lse[(kind, hq, row)] = l
         outs[(kind, hq, row)] = o
         return gq
@@ -105,5 +119,6 @@ def attention_grads(q_cube, k_cube, v_cube, g: Geometry, sel_video: dict, dout_r
         dq[n, hq] = run("v", hq, p, to_f64(q_cube[hq, p]), to_f64(dout_raster[n, hq]), allc)
     for (hq, m), cubes in (sel_extra or {}).items():
         dqx[m, hq] = run("x", hq, m, to_f64(q_extra[m, hq]), to_f64(dout_extra[m, hq]),
-                         [int(j) for j in cubes])
-    return {"dq_raster": dq, "dk_raster": dk, "dv_raster": dv, "dq_extra": dqx, "lse": lse, "o": outs}
+                         [int(j) for j in cubes], m + 1 if n_text else 0)
+    return {"dq_raster": dq, "dk_raster": dk, "dv_raster": dv, "dq_extra": dqx, "dk_text": dkt, "dv_text": dvt,
+            "lse": lse, "o": outs}

@@ -134,3 +134,45 @@ def test_sparse_rows_equal_masked_autograd_and_extra_rows():
     np.testing.assert_allclose(res["dk_raster"][:, 0], k.grad.numpy(), rtol=1e-9, atol=1e-10)
     np.testing.assert_allclose(res["dv_raster"][:, 0], v.grad.numpy(), rtol=1e-9, atol=1e-10)
     np.testing.assert_allclose(res["dq_extra"][:, 0], qxt.grad.numpy(), rtol=1e-9, atol=1e-10)
+
+
+def test_text_rows_with_causal_text_keys_equal_masked_autograd():
+    """Text rows of a prefill attend their selected video cubes and the text
+    tokens up to themselves; the gradients of the text keys and values collect
+    from every later text row (torch autograd over one masked softmax per row)."""
+    wl = workloads.get("tiny").replace(name="tiny_text_grad", n_q_heads=2, n_kv_heads=1, n_text=5, text_kv=True)
+    data = workloads.generate(wl)
+    g = O.Geometry.of(wl)
+    q_cube, _ = O.partition(data["q"], g)
+    k_cube, _ = O.partition(data["k"], g)
+    v_cube, _ = O.partition(data["v"], g)
+    rng = np.random.default_rng(5)
+    nt, Hq, d = wl.n_text, wl.n_q_heads, wl.head_dim
+    dox = rng.standard_normal((nt, Hq, d))
+    selx = {(hq, m): sorted(rng.choice(g.n_cubes, size=2 + m, replace=False).tolist())
+            for hq in range(Hq) for m in range(nt)}
+    qx = O.to_f64(data["q_text"])
+    res = G.attention_grads(q_cube, k_cube, v_cube, g, {}, np.zeros((g.N, Hq, d)), data["q_text"], selx, dox,
+                            k_text=data["k_text"], v_text=data["v_text"])
+    k = torch.tensor(O.to_f64(data["k"])[:, 0], requires_grad=True)
+    v = torch.tensor(O.to_f64(data["v"])[:, 0], requires_grad=True)
+    kt = torch.tensor(O.to_f64(data["k_text"])[:, 0], requires_grad=True)
+    vt = torch.tensor(O.to_f64(data["v_text"])[:, 0], requires_grad=True)
+    qxt = torch.tensor(qx, requires_grad=True)
+    cube, _ = O.cube_coords(g, np.arange(g.N))
+    loss = 0
+    for (hq, m), cubes in selx.items():
+        allowed = torch.tensor(np.concatenate([np.isin(cube, cubes), np.arange(nt) <= m]))
+        keys = torch.cat([k, kt])
+        vals = torch.cat([v, vt])
+        s = (keys @ qxt[m, hq]) / math.sqrt(d)
+        o = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=0) @ vals
+        loss = loss + o @ torch.tensor(dox[m, hq])
+    loss.backward()
+    np.testing.assert_allclose(res["dq_extra"], qxt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dk_raster"][:, 0], k.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dv_raster"][:, 0], v.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dk_text"][:, 0], kt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dv_text"][:, 0], vt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    # the last text key is attended by the last row only
+    assert np.abs(res["dv_text"][-1, 0]).sum() > 0
