@@ -228,14 +228,20 @@ class StreamingCache:
 
 class AdasAttentionGrad:
     """Forward with log-sum-exp and backward of the sparse attention for one
-    layer (video rows, and extra rows that attend their selected cubes only):
-    the fine-tuning step the AdaSpark pages adapt the backbone with.  The
-    selection is computed in the forward and held fixed in the backward."""
+    layer (video rows, and extra rows that attend their selected cubes and,
+    with n_text_kv = n_extra, the causal text keys of a text prefill): the
+    fine-tuning step the AdaSpark pages adapt the backbone with.  The
+    selection is computed in the forward and held fixed in the backward.
+    The text keys' gradients land in ``dk_text`` / ``dv_text``."""
 
     def __init__(self, geom: Geometry, p: float, has_video: bool = True, n_extra: int = 0, device="cuda",
-                 topk: Optional[int] = None):
+                 topk: Optional[int] = None, n_text_kv: int = 0):
+        if n_text_kv not in (0, n_extra):
+            raise ValueError("n_text_kv must be 0 or n_extra")
         self.fwd = AdasAttention(geom, torch.bfloat16, p, has_video=has_video, n_extra=n_extra,
-                                 device=device, topk=topk)
+                                 n_text_kv=n_text_kv, device=device, topk=topk)
+        self.n_text_kv = n_text_kv
+        self._text = (None, None)
         g = geom
         dev = torch.device(device)
         e = dict(device=dev, dtype=torch.bfloat16)
@@ -247,24 +253,32 @@ class AdasAttentionGrad:
         self.dq_extra = torch.empty((n_extra, g.n_q_heads, g.head_dim), **f) if n_extra else None
         self.dk = torch.empty((g.N, g.n_kv_heads, g.head_dim), **f)
         self.dv = torch.empty((g.N, g.n_kv_heads, g.head_dim), **f)
+        self.dk_text = torch.empty((n_text_kv, g.n_kv_heads, g.head_dim), **f) if n_text_kv else None
+        self.dv_text = torch.empty((n_text_kv, g.n_kv_heads, g.head_dim), **f) if n_text_kv else None
         ws = adas_workspace_bytes(g, torch.bfloat16, ADAS_WS_BWD, has_video, n_extra)
         self.ws_bwd = torch.empty((ws,), device=dev, dtype=torch.uint8)
 
-    def forward(self, q_raster, k_raster, v_raster, q_extra=None, stream=None):
+    def forward(self, q_raster, k_raster, v_raster, q_extra=None, stream=None, k_text=None, v_text=None):
+        """k_text / v_text [n_text_kv][Hkv][d]: the text prefill's causal text
+        keys and values (required when n_text_kv > 0)."""
         L = self.fwd
+        if self.n_text_kv and (k_text is None or v_text is None):
+            raise ValueError("this layer has causal text keys: pass k_text and v_text")
+        self._text = (k_text, v_text) if self.n_text_kv else (None, None)
         L.build_kv(k_raster, v_raster, stream)
         adas_cube_partition(L.geom, v_raster, self.v_tok, None, stream)
         adas_cube_partition(L.geom, k_raster, self.k_vt, None, stream, layout=ADAS_LAYOUT_VT)
         if L.has_video:
             L.partition_queries(q_raster, stream)
         L.select(q_extra, stream=stream)
-        adas_sparse_attn_fwd_lse(L.geom, L.q_cube, L.k_cube, L.v_cube, q_extra, None, None, L.sel_count,
-                                 L.sel_idx, L.out_raster, L.out_extra, self.lse, L.ws, stream)
+        adas_sparse_attn_fwd_lse(L.geom, L.q_cube, L.k_cube, L.v_cube, q_extra, self._text[0], self._text[1],
+                                 L.sel_count, L.sel_idx, L.out_raster, L.out_extra, self.lse, L.ws, stream)
         return L.out_raster, L.out_extra
 
     def backward(self, dout_raster, dout_extra=None, q_extra=None, stream=None):
         L = self.fwd
         adas_sparse_attn_bwd(L.geom, L.q_cube, L.k_cube, self.v_tok, self.k_vt, q_extra, L.sel_count, L.sel_idx,
                              L.out_raster, L.out_extra, self.lse, dout_raster, dout_extra, self.dq, self.dq_extra,
-                             self.dk, self.dv, self.ws_bwd, stream)
+                             self.dk, self.dv, self.ws_bwd, stream, k_text=self._text[0], v_text=self._text[1],
+                             dk_text=self.dk_text, dv_text=self.dv_text)
         return self.dq, self.dq_extra, self.dk, self.dv

@@ -90,8 +90,8 @@ def load() -> ctypes.CDLL:
         "adas_cache_sum_bytes": (sz, [gp]),
         "adas_sparse_attn_fwd_lse": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
                                            vp, vp, vp, sz, vp]),
-        "adas_sparse_attn_bwd": (i32, [gp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, vp, vp, vp, sz, vp]),
+        "adas_sparse_attn_bwd": (i32, [gp, i32, vp, vp, vp, vp, i32] + [vp] * 12 + [i32, vp, vp, vp, vp]
+                                 + [vp, sz, vp]),
         "adas_sparse_attn_fwd_noalloc": (i32, [gp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
                                                vp, vp]),
         "adas_probe_mfma": (i32, [i32, i32, vp, ctypes.POINTER(f64), vp]),
@@ -397,9 +397,12 @@ def adas_sparse_attn_fwd_lse(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_
 
 def adas_sparse_attn_bwd(geom: Geometry, q_cube, k_cube, v_tok, k_vt, q_extra, sel_count, sel_idx,
                          out_raster, out_extra, lse, dout_raster, dout_extra, dq_raster, dq_extra,
-                         dk_raster, dv_raster, ws: torch.Tensor, stream=None) -> None:
+                         dk_raster, dv_raster, ws: torch.Tensor, stream=None, k_text=None, v_text=None,
+                         dk_text=None, dv_text=None) -> None:
     """Gradients of the sparse attention with the selection held fixed; see
-    adas.h (bf16 inputs, float32 gradients in raster order)."""
+    adas.h (bf16 inputs, float32 gradients in raster order).  k_text / v_text
+    [n_extra][Hkv][d]: the causal text keys of a text prefill, whose gradients
+    go to dk_text / dv_text."""
     lib = load()
     n_extra = 0 if q_extra is None else q_extra.shape[0]
     Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
@@ -416,6 +419,10 @@ def adas_sparse_attn_bwd(geom: Geometry, q_cube, k_cube, v_tok, k_vt, q_extra, s
     if n_extra:
         _shape(dq_extra, (n_extra, Hq, d), "dq_extra")
         _shape(dout_extra, (n_extra, Hq, d), "dout_extra")
+    n_text_kv = 0 if k_text is None else k_text.shape[0]
+    if n_text_kv:
+        for t, name in ((k_text, "k_text"), (v_text, "v_text"), (dk_text, "dk_text"), (dv_text, "dv_text")):
+            _shape(t, (n_text_kv, Hkv, d), name)
     g, keep = geom._c()
     st = lib.adas_sparse_attn_bwd(
         ctypes.byref(g), ADAS_BF16, _ptr(q_cube, bf, "q_cube"), _ptr(k_cube, bf, "k_cube"), _ptr(v_tok, bf, "v_tok"),
@@ -423,7 +430,9 @@ def adas_sparse_attn_bwd(geom: Geometry, q_cube, k_cube, v_tok, k_vt, q_extra, s
         _ptr(sel_idx, torch.int32, "sel_idx"), _ptr(out_raster, bf, "out_raster"), _ptr(out_extra, bf, "out_extra"),
         _ptr(lse, f32, "lse"), _ptr(dout_raster, bf, "dout_raster"), _ptr(dout_extra, bf, "dout_extra"),
         _ptr(dq_raster, f32, "dq_raster"), _ptr(dq_extra, f32, "dq_extra"), _ptr(dk_raster, f32, "dk_raster"),
-        _ptr(dv_raster, f32, "dv_raster"), _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream))
+        _ptr(dv_raster, f32, "dv_raster"), n_text_kv, _ptr(k_text, bf, "k_text"), _ptr(v_text, bf, "v_text"),
+        _ptr(dk_text, f32, "dk_text"), _ptr(dv_text, f32, "dv_text"), _ptr(ws, name="ws"),
+        ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "adas_sparse_attn_bwd")
 
 

@@ -322,11 +322,16 @@ adas_status adas_sparse_attn_bwd(const adas_geom* geom, adas_dtype dtype, const 
                                  const void* q_extra, const int32_t* sel_count, const int32_t* sel_idx,
                                  const void* out_raster, const void* out_extra, const float* lse,
                                  const void* dout_raster, const void* dout_extra, float* dq_raster,
-                                 float* dq_extra, float* dk_raster, float* dv_raster, void* ws,
-                                 size_t ws_bytes, void* stream) {
+                                 float* dq_extra, float* dk_raster, float* dv_raster, int32_t n_text_kv,
+                                 const void* k_text, const void* v_text, float* dk_text, float* dv_text,
+                                 void* ws, size_t ws_bytes, void* stream) {
   adas::BwdArgs b;
   adas_status st = build_bwd(geom, dtype, q_cube != nullptr, n_extra, b);
   if (st != ADAS_OK) return st;
+  if (n_text_kv != 0 && n_text_kv != n_extra)
+    return fail(ADAS_ERR_VALUE, "n_text_kv must be 0 or n_extra (%d), got %d", n_extra, n_text_kv);
+  if (n_text_kv > 0 && (k_text == nullptr || v_text == nullptr || dk_text == nullptr || dv_text == nullptr))
+    return fail(ADAS_ERR_NULL, "k_text/v_text/dk_text/dv_text is NULL");
   if (k_cube == nullptr || v_tok == nullptr || k_vt == nullptr || sel_count == nullptr || sel_idx == nullptr ||
       lse == nullptr || dk_raster == nullptr || dv_raster == nullptr)
     return fail(ADAS_ERR_NULL, "k_cube/v_tok/k_vt/sel_count/sel_idx/lse/dk_raster/dv_raster is NULL");
@@ -353,6 +358,11 @@ adas_status adas_sparse_attn_bwd(const adas_geom* geom, adas_dtype dtype, const 
   b.dq_extra = dq_extra;
   b.dk_raster = dk_raster;
   b.dv_raster = dv_raster;
+  b.n_text_kv = n_text_kv;
+  b.k_text = (const uint16_t*)k_text;
+  b.v_text = (const uint16_t*)v_text;
+  b.dk_text = dk_text;
+  b.dv_text = dv_text;
   adas::bind_backward_workspace(b, ws);
   return hip_status(adas::launch_backward(b, (hipStream_t)stream), "adas_sparse_attn_bwd launch");
 }

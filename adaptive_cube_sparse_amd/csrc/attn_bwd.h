@@ -25,6 +25,11 @@ struct BwdArgs {
   float* dq_extra;              // [n_extra][Hq][D]
   float* dk_raster;             // [N][Hkv][D]
   float* dv_raster;             // [N][Hkv][D]
+  const uint16_t* k_text;       // [n_text_kv][Hkv][D] causal text keys of a text prefill (or null)
+  const uint16_t* v_text;
+  float* dk_text;               // [n_text_kv][Hkv][D]
+  float* dv_text;
+  int n_text_kv;                // 0, or n_extra: text row m attends text tokens 0..m
   // workspace
   float* delta;                 // [Hq][rows_per_head]: do . o
   uint32_t* bits;               // [Hq][W][rows_per_head]: selection bitmap, word-major

@@ -19,6 +19,10 @@
 //                in LDS and each walks its own 32-row tiles of the block's row
 //                list, with dK^T and dV^T (128 x 64 each) in AGPRs; the waves'
 //                partial sums are added through LDS at the end.
+// With causal text keys (a text prefill: text row m also attends text tokens
+// 0..m), two more: k_bwd_text_dq adds the text keys' share to dq of the text
+// rows, k_bwd_text_dkdv forms the text keys' dK and dV (float32 on the vector
+// ALUs: the text part is a few hundred rows against as many keys).
 #include <type_traits>
 
 #include "attn_bwd.h"
@@ -634,6 +638,165 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// causal text keys: the text row's log-sum-exp L and D = do . o cover its
+// selected cubes and its text keys together, so the text keys' share of the
+// gradients separates:  p_j = exp(c q.k_j - L), ds_j = p_j (do.v_j - D),
+// dq += c sum_j ds_j k_j, dk_j = c sum_rows ds_j q, dv_j = sum_rows p_j do.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kv_group_of(const HeadGroups& hg, int n_groups, int hq) {
+  int grp = 0;
+  for (int gg = 0; gg < n_groups; ++gg)
+    for (int t = hg.start[gg]; t < hg.start[gg + 1]; ++t)
+      if (hg.heads[t] == hq) grp = gg;
+  return grp;
+}
+
+// 16-byte piece of 8 bf16 values as float32
+__device__ __forceinline__ void bf16x8_to_f32(const uint16_t* src, float (&x)[8]) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// One wave per text row (hq, m).  Each round, lane l takes text key j0 + l
+// (j <= m) and forms ds_j from full float32 dot products against the row's q
+// and do (kept in LDS); then every lane adds ds_j k_j over the round's keys to
+// its D/64 output dims.  dq_extra already holds the selected cubes' share.
+template <int D>
+__global__ __launch_bounds__(64) void k_bwd_text_dq(BwdArgs a) {
+  constexpr int PER = D / kWave;
+  __shared__ float s_q[D], s_do[D], s_ds[kWave];
+  const KGeom& g = a.g;
+  const int lane = threadIdx.x;
+  const int hq = blockIdx.x / a.n_extra, m = blockIdx.x - hq * a.n_extra;
+  const int grp = kv_group_of(a.hg, g.Hkv, hq);
+  const int R = a.rows_per_head, Nv = a.has_video ? g.N : 0;
+  const uint16_t* q = a.q_extra + ((size_t)m * g.Hq + hq) * D;
+  const uint16_t* dO = a.dout_extra + ((size_t)m * g.Hq + hq) * D;
+  for (int e = lane; e < D; e += kWave) {
+    s_q[e] = bf16_bits_to_f32(q[e]);
+    s_do[e] = bf16_bits_to_f32(dO[e]);
+  }
+  const float L = a.lse[(size_t)hq * R + Nv + m];
+  const float Dr = a.delta[(size_t)hq * R + Nv + m];
+  const float c = 1.0f / sqrtf((float)D);
+  const size_t kstride = (size_t)g.Hkv * D;  // between consecutive text tokens
+  const uint16_t* kt = a.k_text + (size_t)grp * D;
+  const uint16_t* vt = a.v_text + (size_t)grp * D;
+  __syncthreads();
+  float acc[PER] = {};
+  for (int j0 = 0; j0 <= m; j0 += kWave) {
+    const int j = j0 + lane;
+    float ds = 0.f;
+    if (j <= m) {
+      float sd = 0.f, dp = 0.f;
+      for (int e = 0; e < D; e += 8) {
+        float kx[8], vx[8];
+        bf16x8_to_f32(kt + j * kstride + e, kx);
+        bf16x8_to_f32(vt + j * kstride + e, vx);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sd = fmaf(kx[i], s_q[e + i], sd);
+          dp = fmaf(vx[i], s_do[e + i], dp);
+        }
+      }
+      const float p = expf(c * sd - L);
+      ds = p * (dp - Dr);
+    }
+    s_ds[lane] = ds;
+    __syncthreads();
+    const int nj = min(kWave, m + 1 - j0);
+    for (int jj = 0; jj < nj; ++jj) {
+      const float w = s_ds[jj];
+      const uint16_t* kr = kt + (size_t)(j0 + jj) * kstride + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, bf16_bits_to_f32(kr[i]), acc[i]);
+    }
+    __syncthreads();
+  }
+  float* dst = a.dq_extra + ((size_t)m * g.Hq + hq) * D + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dst[i] += c * acc[i];
+}
+
+// One wave per (KV head, text key j): lanes take the group's text rows m >= j
+// (head slot by head slot) 64 at a time, form p and ds for key j, then every
+// lane folds dv += p do and dk += ds q over the round's rows into its D/64
+// dims.  Every (key, KV head) of the text is written once.
+template <int D>
+__global__ __launch_bounds__(64) void k_bwd_text_dkdv(BwdArgs a) {
+  constexpr int PER = D / kWave;
+  __shared__ float s_k[D], s_v[D], s_p[kWave], s_ds[kWave];
+  __shared__ int s_row[kWave];
+  const KGeom& g = a.g;
+  const int lane = threadIdx.x;
+  const int grp = blockIdx.x / a.n_extra, j = blockIdx.x - grp * a.n_extra;
+  const int R = a.rows_per_head, Nv = a.has_video ? g.N : 0;
+  const int hstart = a.hg.start[grp], gsz = a.hg.start[grp + 1] - hstart;
+  const size_t kstride = (size_t)g.Hkv * D;
+  for (int e = lane; e < D; e += kWave) {
+    s_k[e] = bf16_bits_to_f32(a.k_text[j * kstride + (size_t)grp * D + e]);
+    s_v[e] = bf16_bits_to_f32(a.v_text[j * kstride + (size_t)grp * D + e]);
+  }
+  const float c = 1.0f / sqrtf((float)D);
+  const int per_head = a.n_extra - j;  // text rows j .. n_extra - 1 of each head
+  const int nr = gsz * per_head;
+  __syncthreads();
+  float dk[PER] = {}, dv[PER] = {};
+  for (int r0 = 0; r0 < nr; r0 += kWave) {
+    const int r = r0 + lane;
+    float p = 0.f, ds = 0.f;
+    int hq = 0, m = 0;
+    if (r < nr) {
+      const int slot = r / per_head;
+      m = j + (r - slot * per_head);
+      hq = a.hg.heads[hstart + slot];
+      const uint16_t* q = a.q_extra + ((size_t)m * g.Hq + hq) * D;
+      const uint16_t* dO = a.dout_extra + ((size_t)m * g.Hq + hq) * D;
+      float sd = 0.f, dp = 0.f;
+      for (int e = 0; e < D; e += 8) {
+        float qx[8], ox[8];
+        bf16x8_to_f32(q + e, qx);
+        bf16x8_to_f32(dO + e, ox);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sd = fmaf(qx[i], s_k[e + i], sd);
+          dp = fmaf(ox[i], s_v[e + i], dp);
+        }
+      }
+      p = expf(c * sd - a.lse[(size_t)hq * R + Nv + m]);
+      ds = p * (dp - a.delta[(size_t)hq * R + Nv + m]);
+    }
+    s_p[lane] = p;
+    s_ds[lane] = ds;
+    s_row[lane] = m * g.Hq + hq;
+    __syncthreads();
+    const int nrr = min(kWave, nr - r0);
+    for (int rr = 0; rr < nrr; ++rr) {
+      const size_t off = (size_t)s_row[rr] * D + lane * PER;
+      const float pw = s_p[rr], dw = s_ds[rr];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        dv[i] = fmaf(pw, bf16_bits_to_f32(a.dout_extra[off + i]), dv[i]);
+        dk[i] = fmaf(dw, bf16_bits_to_f32(a.q_extra[off + i]), dk[i]);
+      }
+    }
+    __syncthreads();
+  }
+  float* dko = a.dk_text + (j * kstride + (size_t)grp * D) + lane * PER;
+  float* dvo = a.dv_text + (j * kstride + (size_t)grp * D) + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    dko[i] = c * dk[i];
+    dvo[i] = dv[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------
 void plan_backward(BwdArgs& a) {
@@ -681,12 +844,20 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
                        0, s, a);
     hipLaunchKernelGGL(k_bwd_lists, dim3(g.Hkv * g.Nc), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_bwd_dkdv<128>, dim3(g.Nc * g.Hkv * nkb), dim3(256), 0, s, a);
+    if (a.n_text_kv > 0) {
+      hipLaunchKernelGGL(k_bwd_text_dq<128>, dim3(g.Hq * a.n_extra), dim3(64), 0, s, a);
+      hipLaunchKernelGGL(k_bwd_text_dkdv<128>, dim3(g.Hkv * a.n_extra), dim3(64), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL(k_bwd_prep<64>, dim3((rows + 15) / 16), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_bwd_dq<64>, dim3(a.n_extra_tiles + g.Hkv * a.video_tiles_per_group), dim3(BNT),
                        0, s, a);
     hipLaunchKernelGGL(k_bwd_lists, dim3(g.Hkv * g.Nc), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_bwd_dkdv<64>, dim3(g.Nc * g.Hkv * nkb), dim3(256), 0, s, a);
+    if (a.n_text_kv > 0) {
+      hipLaunchKernelGGL(k_bwd_text_dq<64>, dim3(g.Hq * a.n_extra), dim3(64), 0, s, a);
+      hipLaunchKernelGGL(k_bwd_text_dkdv<64>, dim3(g.Hkv * a.n_extra), dim3(64), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

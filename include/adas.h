@@ -252,8 +252,9 @@ adas_status adas_sparse_attn_fwd_lse(const adas_geom* geom, adas_dtype dtype, co
  * on the sparse pattern (papernotes.org, training strategy; key design 2
  * attention).  The selection is a discrete choice and is held fixed: no
  * gradient reaches it or the mean keys.  Rows: video rows (selected cubes +
- * own cube) and extra rows (selected cubes only; the causal text keys of a
- * text prefill are not covered).  bf16 only, cubes of S = 64 tokens.
+ * own cube) and extra rows (selected cubes, and with n_text_kv = n_extra the
+ * causal text keys of a text prefill, as the forward reads them).  bf16 only,
+ * cubes of S = 64 tokens.
  *   q_cube, k_cube [h][NS][d]      ADAS_LAYOUT_TOKENS (q_cube NULL: no video rows)
  *   v_tok    [Hkv][NS][d]          V in ADAS_LAYOUT_TOKENS
  *   k_vt     [Hkv][NS/S][d][S]     K in ADAS_LAYOUT_VT
@@ -263,17 +264,24 @@ adas_status adas_sparse_attn_fwd_lse(const adas_geom* geom, adas_dtype dtype, co
  *   dq_raster [N][Hq][d], dq_extra [n_extra][Hq][d],
  *   dk_raster, dv_raster [N][Hkv][d]   float32 outputs, raster token order;
  *            every element is written (keys no row attends get 0)
+ *   n_text_kv  0, or n_extra for a text prefill whose extra rows are text
+ *            tokens with causal text keys (the forward's n_text_kv)
+ *   k_text, v_text [n_text_kv][Hkv][d]  the forward's text keys and values
+ *   dk_text, dv_text [n_text_kv][Hkv][d]  float32 outputs, every element
+ *            written (NULL, with k_text and v_text, when n_text_kv = 0)
  *   ws, ws_bytes  adas_workspace_bytes(ADAS_WS_BWD, ...): per-row D, the
  *            selections as bitmaps, and per cube the list of rows attending it
- * Errors: NULL, SHAPE (S != 64, Nc), DTYPE (not bf16), WORKSPACE, HIP.
+ * Errors: NULL, SHAPE (S != 64, Nc), VALUE (n_text_kv not 0 or n_extra),
+ *         DTYPE (not bf16), WORKSPACE, HIP.
  */
 adas_status adas_sparse_attn_bwd(const adas_geom* geom, adas_dtype dtype, const void* q_cube,
                                  const void* k_cube, const void* v_tok, const void* k_vt, int32_t n_extra,
                                  const void* q_extra, const int32_t* sel_count, const int32_t* sel_idx,
                                  const void* out_raster, const void* out_extra, const float* lse,
                                  const void* dout_raster, const void* dout_extra, float* dq_raster,
-                                 float* dq_extra, float* dk_raster, float* dv_raster, void* ws,
-                                 size_t ws_bytes, void* stream);
+                                 float* dq_extra, float* dk_raster, float* dv_raster, int32_t n_text_kv,
+                                 const void* k_text, const void* v_text, float* dk_text, float* dv_text,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * adas_cache_append -- grow a video KV cache while decoding: frames arrive in

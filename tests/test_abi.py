@@ -189,6 +189,30 @@ def test_attention_and_partition_reject_invalid_arguments_on_host():
     assert attn(q_cube=None, out=None, n_extra=2, q_extra=FAKE, out_x=FAKE) == L.ADAS_ERR_WORKSPACE
 
 
+def test_backward_rejects_invalid_arguments_on_host():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    g = _geom()  # cubes of 64 tokens
+
+    def bwd(geom=g, **kw):
+        a = dict(q_cube=FAKE, n_extra=0, q_extra=None, out_x=None, dout_x=None, dq_x=None, ntk=0, kt=None,
+                 vt=None, dkt=None, dvt=None, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.adas_sparse_attn_bwd(ctypes.byref(geom), L.ADAS_BF16, a["q_cube"], FAKE, FAKE, FAKE,
+                                        a["n_extra"], a["q_extra"], FAKE, FAKE, FAKE, a["out_x"], FAKE, FAKE,
+                                        a["dout_x"], FAKE, a["dq_x"], FAKE, FAKE, a["ntk"], a["kt"], a["vt"],
+                                        a["dkt"], a["dvt"], a["ws"], a["ws_bytes"], None)
+    text = dict(n_extra=4, q_extra=FAKE, out_x=FAKE, dout_x=FAKE, dq_x=FAKE)
+    assert bwd(**text, ntk=3) == L.ADAS_ERR_VALUE               # text keys must match the extra rows
+    assert "n_text_kv" in lib.adas_last_error().decode()
+    assert bwd(**text, ntk=4, kt=FAKE, vt=FAKE, dkt=None, dvt=FAKE) == L.ADAS_ERR_NULL
+    assert bwd(**text, ntk=4, kt=None, vt=FAKE, dkt=FAKE, dvt=FAKE) == L.ADAS_ERR_NULL
+    assert bwd(ntk=1) == L.ADAS_ERR_VALUE                        # no extra rows, no text keys
+    assert bwd(ws=None) == L.ADAS_ERR_WORKSPACE
+    assert bwd(geom=_geom(ct=2, ch=8, cw=8)) == L.ADAS_ERR_SHAPE  # cubes of 128: disabled
+    assert bwd(q_cube=None) == L.ADAS_ERR_SHAPE                  # no rows at all
+
+
 def _ffn_geom(**kw):
     import adaptive_cube_sparse_amd._lib as L
     base = dict(T=4, H=8, W=8, ct=2, ch=4, cw=4, hidden=256, inter=384)

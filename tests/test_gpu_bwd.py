@@ -50,7 +50,7 @@ def _lists(layer, wl, g, video_rows=None):
     cnt = layer.sel_count.cpu().numpy()
     idx = layer.sel_idx.cpu().numpy()
     capv = g.S * g.n_cubes * (g.n_cubes - 1) // 2 if wl.video_queries else 0
-    n_extra = wl.n_decode
+    n_extra = wl.n_text + wl.n_decode
     sv, sx = {}, {}
     if video_rows is not None:
         for hq, p in video_rows:
@@ -85,19 +85,23 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
     of them is listed)."""
     from adaptive_cube_sparse_amd import AdasAttentionGrad
     p = wl.p if p is None else p
+    n_extra = wl.n_text + wl.n_decode
+    n_tk = wl.n_text if wl.text_kv else 0
     log(f"[bwd] {wl.name} grid {wl.T}x{wl.H}x{wl.W} cube ({wl.ct},{wl.ch},{wl.cw}) heads {wl.n_q_heads}/"
-        f"{wl.n_kv_heads} d {wl.head_dim} p {p} extra {wl.n_decode}")
+        f"{wl.n_kv_heads} d {wl.head_dim} p {p} extra {n_extra} causal text keys {n_tk}")
     data = workloads.generate(wl)
     g = O.Geometry.of(wl)
     dev = "cuda:0"
     rng = np.random.default_rng(seed)
-    n_extra = wl.n_decode
     dout = _bf16_normal(rng, (g.N, wl.n_q_heads, wl.head_dim)) if wl.video_queries else None
     doutx = _bf16_normal(rng, (n_extra, wl.n_q_heads, wl.head_dim)) if n_extra else None
-    layer = AdasAttentionGrad(_geom(wl), p, has_video=wl.video_queries, n_extra=n_extra, device=dev)
+    layer = AdasAttentionGrad(_geom(wl), p, has_video=wl.video_queries, n_extra=n_extra, device=dev,
+                              n_text_kv=n_tk)
     qx = to_dev(data["q_text"], dev) if n_extra else None
+    kt = to_dev(data["k_text"], dev) if n_tk else None
+    vt = to_dev(data["v_text"], dev) if n_tk else None
     layer.forward(to_dev(data["q"], dev) if wl.video_queries else None, to_dev(data["k"], dev),
-                  to_dev(data["v"], dev), qx)
+                  to_dev(data["v"], dev), qx, k_text=kt, v_text=vt)
     dq, dqx, dk, dv = layer.backward(to_dev(dout, dev) if dout is not None else None,
                                      to_dev(doutx, dev) if doutx is not None else None, qx)
     torch.cuda.synchronize()
@@ -106,7 +110,8 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
     k_cube, _ = O.partition(data["k"], g)
     v_cube, _ = O.partition(data["v"], g)
     ref = G.attention_grads(q_cube, k_cube, v_cube, g, sv, dout if dout is not None else np.zeros((g.N, wl.n_q_heads, wl.head_dim)),
-                            data.get("q_text"), sx, doutx)
+                            data.get("q_text"), sx, doutx, k_text=data.get("k_text") if n_tk else None,
+                            v_text=data.get("v_text") if n_tk else None)
     # log-sum-exp
     lse = layer.lse.cpu().numpy()
     lerr = 0.0
@@ -135,8 +140,11 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
             cubes = sx[(hq, r)]
             qv, dov, od = O.to_f64(data["q_text"][r, hq]), O.to_f64(doutx[r, hq]), outx_dev[r, hq]
             want = ref["dq_extra"][r, hq]
-        pos = np.concatenate([np.arange(j * g.S, (j + 1) * g.S) for j in cubes])
+        pos = np.concatenate([np.arange(j * g.S, (j + 1) * g.S) for j in cubes]) if cubes else np.zeros(0, int)
         keys, vals = O.to_f64(k_cube[kv][pos]), O.to_f64(v_cube[kv][pos])
+        if kind == "x" and n_tk:  # text row r also attends text tokens 0..r
+            keys = np.concatenate([keys, O.to_f64(data["k_text"][:r + 1, kv])])
+            vals = np.concatenate([vals, O.to_f64(data["v_text"][:r + 1, kv])])
         pw, ds = G.row_weights(qv, keys, vals, dov)
         bound = cs * u * (np.abs(dov * od).sum() * np.abs(pw @ keys) + np.abs(ds) @ np.abs(keys)) \
             + 2e-3 * np.abs(want) + 1e-4 * np.sqrt(np.mean(want ** 2))
@@ -151,6 +159,9 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
         keys = np.sort(np.concatenate([perm[j * g.S:(j + 1) * g.S] for j in key_cubes]))
     errs["dk"] = _err(dk.cpu().numpy()[keys], ref["dk_raster"][keys])
     errs["dv"] = _err(dv.cpu().numpy()[keys], ref["dv_raster"][keys])
+    if n_tk:
+        errs["dk_text"] = _err(layer.dk_text.cpu().numpy(), ref["dk_text"])
+        errs["dv_text"] = _err(layer.dv_text.cpu().numpy(), ref["dv_text"])
     log("  lse max-abs %.2e; " % lerr + ", ".join(f"{k}: max {e.max():.2e} mean {e.mean():.2e}" for k, e in errs.items()))
     assert lerr <= 1e-3
     for k, e in errs.items():
@@ -182,6 +193,18 @@ def test_bwd_cubes_of_128_two_key_blocks():
 
 def test_bwd_extra_rows_only():
     _run_case(_small(name="bwd_extra", video_queries=False, n_decode=40, seed=4104), p=0.5)
+
+
+def test_bwd_text_rows_with_causal_text_keys():
+    # a text prefill: 20 text rows attend their selected cubes and the text
+    # tokens up to themselves, next to the video rows
+    _run_case(_small(name="bwd_text", n_text=20, text_kv=True, seed=4107))
+
+
+def test_bwd_text_only_prefill_two_text_key_rounds():
+    # no video rows; 70 text rows (the text kernels' rounds of 64 keys and
+    # rows end in a partial round)
+    _run_case(_small(name="bwd_text_only", video_queries=False, n_text=70, text_kv=True, seed=4108), p=0.5)
 
 
 def test_bwd_many_cubes_and_tiles():
