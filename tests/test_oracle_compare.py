@@ -1,4 +1,4 @@
-"""Pins for the grader that decides every device Top-p / Top-K verdict
+"""Pins for the grader that grades every device Top-p / Top-K selection
 (``oracle/compare.py``).
 
 The rule it grades against: papernotes.org, AdaSpark, key design 2 (S_i =
