@@ -54,7 +54,7 @@ def device_signatures(layer, ref):
     return cnt.cpu().numpy(), sig.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["qwen3b", "qwen7b_p07", "hour", "decode"])
+@pytest.mark.parametrize("name", ["qwen3b", "qwen7b_p05", "qwen7b_p07", "qwen7b_p09", "hour", "decode"])
 def test_full_selection_lists(name):
     wl = workloads.get(name)
     log(f"case {name}: full selection check, {wl.n_q_heads} heads, p {wl.p}")
