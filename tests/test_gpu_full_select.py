@@ -1,4 +1,5 @@
-"""Full-size layers: every row's Top-p list against the oracle (not a sample).
+"""Full-size layers, and a layer at the cube limit: every row's Top-p list
+against the oracle (not a sample).
 
 The oracle's whole-layer selection runs in worker processes (one task per
 query head); the device lists are reduced to per-row signatures on the GPU
@@ -16,8 +17,8 @@ import pytest
 import workloads
 from oracle.compare import grade_row
 from tests.full_select import oracle_signatures, tags
-from tests.gpu_harness import ALARM_FRAC, Reference, check_layout, fetch_lists, log, run_device, \
-    selection_probs
+from tests.gpu_harness import ALARM_FRAC, Reference, check_layout, check_rows, fetch_lists, log, \
+    run_device, sampled_rows, selection_probs
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +55,19 @@ def device_signatures(layer, ref):
     return cnt.cpu().numpy(), sig.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["qwen3b", "qwen7b_p05", "qwen7b_p07", "qwen7b_p09", "hour", "decode"])
+# The cube limit (ADAS_MAX_CUBES = 4096, cubes of 16 tokens) with video rows:
+# query cubes past 1024 and 2048 run the 32- and 64-slot selection bands that
+# the configurations above never reach, and the text rows (4096 candidates)
+# ride in the 64-slot band.
+MAX_CUBES = workloads.Workload(name="max_cubes", T=256, H=16, W=16, ct=1, ch=4, cw=4, n_q_heads=2,
+                               n_kv_heads=1, head_dim=64, dtype="bf16", p=0.6, seed=48,
+                               n_text=4, text_kv=True)
+
+
+@pytest.mark.parametrize("name", ["qwen3b", "qwen7b_p05", "qwen7b_p07", "qwen7b_p09", "hour", "decode",
+                                  "max_cubes"])
 def test_full_selection_lists(name):
-    wl = workloads.get(name)
+    wl = MAX_CUBES if name == "max_cubes" else workloads.get(name)
     log(f"case {name}: full selection check, {wl.n_q_heads} heads, p {wl.p}")
     data = workloads.generate(wl)
     layer = run_device(wl, data)
@@ -80,3 +91,6 @@ def test_full_selection_lists(name):
     log(f"  grades over all {oc.size} rows: {grades}; oracle rows within 1e-5 of p: {int(near.sum())}")
     assert grades["fail"] == 0, f"selection failures: {fails}"
     assert grades["near_threshold"] + grades["near_tie"] <= max(2, ALARM_FRAC * oc.size)
+    if name == "max_cubes":
+        # outputs of this layer on a stratified sample of rows
+        check_rows(ref, layer, sampled_rows(ref, cubes_per_decile=2, tokens_per_cube=4), wl.p)

@@ -162,6 +162,29 @@ def test_text_prefill_without_video_rows():
     _case(wl)
 
 
+def test_max_query_heads_with_text_rows():
+    # the largest head count the library takes (ADAS_MAX_HEADS = 128 query
+    # heads) over 2 KV heads: 64 query heads per group, so each query cube's
+    # rows of a group fill 8 union tiles, and 5 text rows per head give 320
+    # extra rows per group (a full extra-row tile and a partial one)
+    wl = workloads.Workload(name="max_heads", T=4, H=8, W=8, ct=2, ch=4, cw=4, n_q_heads=128,
+                            n_kv_heads=2, head_dim=64, dtype="bf16", p=0.7, seed=46,
+                            n_text=5, text_kv=True)
+    _case(wl)
+
+
+def test_single_cube_layer():
+    # one cube of 256 tokens (Nc = 1): no video row has a candidate, so every
+    # video row attends its own cube only and its list is empty; each text row
+    # has the one cube as its only candidate (P = 1), so it selects it
+    wl = workloads.Workload(name="one_cube", T=4, H=8, W=8, ct=4, ch=8, cw=8, n_q_heads=4,
+                            n_kv_heads=2, head_dim=128, dtype="bf16", p=0.7, seed=47,
+                            n_text=3, text_kv=True)
+    ref, layer = _case(wl)
+    cnt = layer.sel_count.cpu().numpy()
+    assert (cnt[:, :ref.g.N] == 0).all() and (cnt[:, ref.g.N:] == 1).all()
+
+
 def test_deterministic():
     data = workloads.generate(SMALL)
     a = run_device(SMALL, data)
