@@ -375,34 +375,49 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // ALUs; PV(u): its MFMAs into the output (D/16 each).  The units of one or two blocks
   // run as steps S(0); S(1)|sm(0); S(2) PV(0)|sm(1); S(3) PV(1)|sm(2);
   // PV(2)|sm(3); PV(3).  Within a step the order is fixed by scheduling
-  // barriers: slot k issues the LDS operand read of MFMA k+2, MFMA k, then a
+  // barriers: slot k issues the LDS operand read of MFMA k+3, MFMA k, then a
   // slice of the softmax, so the exp and convert instructions of one unit run
-  // while the MFMAs of its neighbours execute.  Scores and probabilities
+  // while the MFMAs of its neighbours execute.  The last three slots of a step
+  // read the first three operands of the next step of the same blocks, so a
+  // step starts with its operands in flight.  Scores and probabilities
   // alternate between two register slots (u % 2); S and PV MFMAs of a step
   // alternate, so consecutive MFMAs use different accumulators.
   f32x16 su[2];
   bf16x8u pu[2][2];
+  uint4 fq[4];  // LDS operand fragments in flight: MFMA k of a step reads fq[k % 4]
+  // operand read of MFMA k of a step with score unit sU and output unit pvU
+  auto rd_op = [&](auto sUc, auto pvUc, auto kc, const uint16_t* kb, const uint16_t* vb)
+                   __attribute__((always_inline)) {
+    constexpr int sU = decltype(sUc)::value, pvU = decltype(pvUc)::value, k = decltype(kc)::value;
+    constexpr bool HS = sU >= 0, HP = pvU >= 0;
+    constexpr bool is_s = HS && (!HP || k % 2 == 0);
+    constexpr int i = (HS && HP) ? k / 2 : k;
+    constexpr int ND = D / 32;
+    if constexpr (is_s)
+      fq[k % 4] = *reinterpret_cast<const uint4*>(&kb[(32 * (sU & 1) + lr) * Sm::KS + 16 * i + 8 * lh]);
+    else
+      fq[k % 4] = *reinterpret_cast<const uint4*>(
+          &vb[(32 * (i % ND) + lr) * Sm::VS + 16 * (2 * (pvU & 1) + i / ND) + 8 * lh]);
+  };
+  // run_step(S unit, PV unit, softmax unit, K / V^T buffers, rows selected,
+  //          operands already read by the previous step, next step's S and PV
+  //          units (UN, UN: none), next step's buffers)
   auto run_step = [&](auto sUc, auto pvUc, auto smUc, const uint16_t* kb, const uint16_t* vb,
-                      bool sel) __attribute__((always_inline)) {
+                      bool sel, auto preC, auto nsUc, auto npvUc, const uint16_t* kbn,
+                      const uint16_t* vbn) __attribute__((always_inline)) {
     constexpr int sU = decltype(sUc)::value, pvU = decltype(pvUc)::value, smU = decltype(smUc)::value;
     constexpr bool HS = sU >= 0, HP = pvU >= 0, HM = smU >= 0;
     constexpr int NO = D / 16;  // MFMAs of one S(u) (k-steps over d) and of one PV(u) (2 k-steps x D/32 tiles)
     constexpr int ND = D / 32;
     constexpr int NM = (HS ? NO : 0) + (HP ? NO : 0);
+    constexpr int NNM = (decltype(nsUc)::value >= 0 ? NO : 0) + (decltype(npvUc)::value >= 0 ? NO : 0);
+    static_assert(NM % 4 == 0, "a step's MFMA count keeps the fragment slots aligned");
     constexpr int ss = sU & 1, ps = pvU & 1, ms = smU & 1;
-    uint4 f[3];
     auto is_s = [](auto kc) constexpr { return HS && (!HP || (decltype(kc)::value % 2) == 0); };
     auto op_i = [](auto kc) constexpr { return (HS && HP) ? decltype(kc)::value / 2 : decltype(kc)::value; };
-    auto rd = [&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value, i = op_i(kc);
-      if constexpr (is_s(kc))
-        f[k % 3] = *reinterpret_cast<const uint4*>(&kb[(32 * ss + lr) * Sm::KS + 16 * i + 8 * lh]);
-      else
-        f[k % 3] = *reinterpret_cast<const uint4*>(&vb[(32 * (i % ND) + lr) * Sm::VS + 16 * (2 * ps + i / ND) + 8 * lh]);
-    };
     auto mf = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value, i = op_i(kc);
-      const bf16x8u a8 = __builtin_bit_cast(bf16x8u, f[k % 3]);
+      const bf16x8u a8 = __builtin_bit_cast(bf16x8u, fq[k % 4]);
       if constexpr (is_s(kc)) {
         if constexpr (i == 0) {
           const f32x16 z = {};
@@ -431,12 +446,17 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       const bf16x2u pair = {p0, p1};
       ls = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, ls, false);
     };
-    if constexpr (NM > 0) rd(std::integral_constant<int, 0>{});
-    if constexpr (NM > 1) rd(std::integral_constant<int, 1>{});
+    if constexpr (!decltype(preC)::value) {
+      rd_op(sUc, pvUc, std::integral_constant<int, 0>{}, kb, vb);
+      rd_op(sUc, pvUc, std::integral_constant<int, 1>{}, kb, vb);
+      rd_op(sUc, pvUc, std::integral_constant<int, 2>{}, kb, vb);
+    }
     static_for<0, NM>([&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (k + 2 < NM) rd(std::integral_constant<int, k + 2>{});
+      if constexpr (k + 3 < NM) rd_op(sUc, pvUc, std::integral_constant<int, k + 3>{}, kb, vb);
+      else if constexpr (k + 3 - NM < NNM)
+        rd_op(nsUc, npvUc, std::integral_constant<int, k + 3 - NM>{}, kbn, vbn);
       mf(kc);
       if constexpr (HM)
         static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
@@ -486,21 +506,23 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using U2 = std::integral_constant<int, 2>;
   using U3 = std::integral_constant<int, 3>;
   // one full block
+  using PF = std::false_type;
+  using PT = std::true_type;
   auto block1 = [&](const uint16_t* kb, const uint16_t* vb, bool sel) __attribute__((always_inline)) {
-    run_step(U0{}, UN{}, UN{}, kb, vb, sel);
-    run_step(U1{}, UN{}, U0{}, kb, vb, sel);
-    run_step(UN{}, U0{}, U1{}, kb, vb, sel);
-    run_step(UN{}, U1{}, UN{}, kb, vb, sel);
+    run_step(U0{}, UN{}, UN{}, kb, vb, sel, PF{}, U1{}, UN{}, kb, vb);
+    run_step(U1{}, UN{}, U0{}, kb, vb, sel, PT{}, UN{}, U0{}, kb, vb);
+    run_step(UN{}, U0{}, U1{}, kb, vb, sel, PT{}, UN{}, U1{}, kb, vb);
+    run_step(UN{}, U1{}, UN{}, kb, vb, sel, PT{}, UN{}, UN{}, kb, vb);
   };
   // two full blocks
   auto block2 = [&](const uint16_t* kb0, const uint16_t* vb0, bool sel0, const uint16_t* kb1,
                     const uint16_t* vb1, bool sel1) __attribute__((always_inline)) {
-    run_step(U0{}, UN{}, UN{}, kb0, vb0, sel0);
-    run_step(U1{}, UN{}, U0{}, kb0, vb0, sel0);
-    run_step(U2{}, U0{}, U1{}, kb1, vb0, sel0);
-    run_step(U3{}, U1{}, U2{}, kb1, vb0, sel1);
-    run_step(UN{}, U2{}, U3{}, kb1, vb1, sel1);
-    run_step(UN{}, U3{}, UN{}, kb1, vb1, sel1);
+    run_step(U0{}, UN{}, UN{}, kb0, vb0, sel0, PF{}, U1{}, UN{}, kb0, vb0);
+    run_step(U1{}, UN{}, U0{}, kb0, vb0, sel0, PT{}, U2{}, U0{}, kb1, vb0);
+    run_step(U2{}, U0{}, U1{}, kb1, vb0, sel0, PT{}, U3{}, U1{}, kb1, vb0);
+    run_step(U3{}, U1{}, U2{}, kb1, vb0, sel1, PT{}, UN{}, U2{}, kb1, vb1);
+    run_step(UN{}, U2{}, U3{}, kb1, vb1, sel1, PT{}, UN{}, U3{}, kb1, vb1);
+    run_step(UN{}, U3{}, UN{}, kb1, vb1, sel1, PT{}, UN{}, UN{}, kb1, vb1);
   };
 
   // Register-staged walk over nb key blocks: source(i, kptr, vptr, stride, kc)
@@ -594,20 +616,30 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   // barrier before blocks i, i+1 every wave is done with blocks i-2, i-1, so
   // their buffers take blocks i+2, i+3.  The loop is unrolled over both
   // buffer pairs so that every buffer is named at compile time.
-  auto dpipeline = [&](int nb, auto bsrc, auto work) __attribute__((always_inline)) {
+  // The union list and mask lookups run one pair ahead: at pair i the wave
+  // reads the masks of blocks i+2, i+3 and the list entries of blocks i+4,
+  // i+5, which it uses only at the next pair, so no LDS round trip sits
+  // between the barrier and the first MFMA.  ul_read(i): list entry of block
+  // i (any i; beyond the list it names an in-bounds stale entry, which is
+  // never used to load); offs(i, ul, ko, vo): block i's byte offsets;
+  // mask_read(ul): this wave's row mask of a list entry.
+  auto dpipeline = [&](int nb, auto ul_read, auto offs, auto mask_read, auto work) __attribute__((always_inline)) {
     if (nb <= 0) return;
     __syncthreads();  // the previous phase no longer reads any buffer
-    auto issue_block = [&](int i, auto bufc) __attribute__((always_inline)) {
+    auto issue_ul = [&](int i, int ul, auto bufc) __attribute__((always_inline)) {
       if (i < nb) {
         uint32_t ko, vo;
-        bsrc(i, ko, vo);
+        offs(i, ul, ko, vo);
         issue(ko, vo, bufc);
       }
     };
-    issue_block(0, C0{});
-    issue_block(1, C1{});
-    issue_block(2, C2{});
-    issue_block(3, C3{});
+    const int ul0 = ul_read(0), ul1 = ul_read(1);
+    int ua0 = ul_read(2), ua1 = ul_read(3);  // list entries of blocks i+2, i+3
+    issue_ul(0, ul0, C0{});
+    issue_ul(1, ul1, C1{});
+    issue_ul(2, ua0, C2{});
+    issue_ul(3, ua1, C3{});
+    uint32_t mw0 = mask_read(ul0), mw1 = mask_read(ul1);  // masks of blocks i, i+1
     auto pair = [&](auto b0, auto b1, auto n0, auto n1, int i) __attribute__((always_inline)) {
       // blocks i, i+1 must have landed.  At i = 0 the loads of blocks 2 and 3
       // (those that exist) may stay in flight: a wave issues NLMIN or NLMIN+1
@@ -619,10 +651,16 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (i >= 2) {
-        issue_block(i + 2, n0);
-        issue_block(i + 3, n1);
+        issue_ul(i + 2, ua0, n0);
+        issue_ul(i + 3, ua1, n1);
       }
-      work(i, kbuf_c(b0), vbuf_c(b0), kbuf_c(b1), vbuf_c(b1), i + 1 < nb);
+      const uint32_t nm0 = mask_read(ua0), nm1 = mask_read(ua1);
+      const int nu0 = ul_read(i + 4), nu1 = ul_read(i + 5);
+      work(i, kbuf_c(b0), vbuf_c(b0), kbuf_c(b1), vbuf_c(b1), mw0, i + 1 < nb ? mw1 : 0u);
+      mw0 = nm0;
+      mw1 = nm1;
+      ua0 = nu0;
+      ua1 = nu1;
     };
     for (int i = 0; i < nb; i += 4) {
       pair(C0{}, C1{}, C2{}, C3{}, i);
@@ -773,14 +811,16 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       const int nblk = s_nunion * nkb_cube;
       dpipeline(
           nblk,
-          [&](int i, uint32_t& ko, uint32_t& vo) __attribute__((always_inline)) {
-            const int ci = i / nkb_cube, kbi = i - ci * nkb_cube;
-            const int j = __builtin_amdgcn_readfirstlane(jb + s_ulist[ci]);
+          [&](int i) __attribute__((always_inline)) { return (int)s_ulist[min(i / nkb_cube, UPASS - 1)]; },
+          [&](int i, int ul, uint32_t& ko, uint32_t& vo) __attribute__((always_inline)) {
+            const int kbi = i - (i / nkb_cube) * nkb_cube;
+            const int j = __builtin_amdgcn_readfirstlane(jb + ul);
             ko = (uint32_t)(((size_t)j * g.S + kbi * UKB) * D * 2);
             vo = (uint32_t)((size_t)j * g.S * D * 2 + kbi * UKB * 2);
           },
+          [&](int ul) __attribute__((always_inline)) { return s_bits[UNW * min(ul, UPASS - 1) + wave]; },
           [&](int i, const uint16_t* kb0, const uint16_t* vb0, const uint16_t* kb1, const uint16_t* vb1,
-              bool two) __attribute__((always_inline)) {
+              uint32_t mw0, uint32_t mw1) __attribute__((always_inline)) {
             // this wave's row masks of blocks i and i+1.  Every pair runs the
             // two-block path, with no skipping (in union tiles a wave whose 32
             // rows all pass over a block is rare): one code path keeps the
@@ -789,8 +829,6 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
             // zeroed at the start) contents, every row masked.  A wave that
             // holds no rows (possible in a head's last tile) skips every pair.
             if (!wave_has_rows) return;
-            const uint32_t mw0 = s_bits[UNW * s_ulist[i / nkb_cube] + wave];
-            const uint32_t mw1 = two ? s_bits[UNW * s_ulist[(i + 1) / nkb_cube] + wave] : 0u;
             const bool sel0 = ((mw0 >> lr) & 1u) != 0u, sel1 = ((mw1 >> lr) & 1u) != 0u;
             block2(kb0, vb0, sel0, kb1, vb1, sel1);
           });
