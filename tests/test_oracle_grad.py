@@ -176,3 +176,60 @@ def test_text_rows_with_causal_text_keys_equal_masked_autograd():
     np.testing.assert_allclose(res["dv_text"][:, 0], vt.grad.numpy(), rtol=1e-9, atol=1e-10)
     # the last text key is attended by the last row only
     assert np.abs(res["dv_text"][-1, 0]).sum() > 0
+
+
+def test_head_map_routes_every_gradient_to_its_kv_head():
+    """Grouped heads with an explicit, non-monotone head map ([1, 0, 1]: query
+    heads 0 and 2 read KV head 1): video rows and text rows with causal text
+    keys, against torch autograd over one masked softmax per (head, row) that
+    reads the mapped KV head, so dK / dV of each KV head collect exactly the
+    rows of its query heads."""
+    wl = workloads.get("tiny").replace(name="tiny_head_map_grad", n_q_heads=3, n_kv_heads=2, n_text=3,
+                                       text_kv=True)
+    hm = [1, 0, 1]
+    data = workloads.generate(wl)
+    g = O.Geometry.of(wl)
+    q_cube, perm = O.partition(data["q"], g)
+    k_cube, _ = O.partition(data["k"], g)
+    v_cube, _ = O.partition(data["v"], g)
+    rng = np.random.default_rng(6)
+    Hq, d, nt = wl.n_q_heads, wl.head_dim, wl.n_text
+    rows = [(hq, int(p)) for hq in range(Hq) for p in rng.choice(g.N, size=12, replace=False)]
+    sel = {(hq, p): sorted(rng.choice(max(p // g.S, 1), size=min(2, p // g.S), replace=False).tolist())
+           for hq, p in rows}
+    selx = {(hq, m): sorted(rng.choice(g.n_cubes, size=2, replace=False).tolist()) for hq in range(Hq)
+            for m in range(nt)}
+    dout = rng.standard_normal((g.N, Hq, d))
+    dox = rng.standard_normal((nt, Hq, d))
+    res = G.attention_grads(q_cube, k_cube, v_cube, g, sel, dout, data["q_text"], selx, dox, head_map=hm,
+                            k_text=data["k_text"], v_text=data["v_text"])
+    k = torch.tensor(O.to_f64(data["k"]), requires_grad=True)          # [N][Hkv][d]
+    v = torch.tensor(O.to_f64(data["v"]), requires_grad=True)
+    kt = torch.tensor(O.to_f64(data["k_text"]), requires_grad=True)    # [nt][Hkv][d]
+    vt = torch.tensor(O.to_f64(data["v_text"]), requires_grad=True)
+    qr = torch.tensor(O.to_f64(data["q"]), requires_grad=True)         # [N][Hq][d]
+    qxt = torch.tensor(O.to_f64(data["q_text"]), requires_grad=True)   # [nt][Hq][d]
+    cube, _ = O.cube_coords(g, np.arange(g.N))
+    loss = 0
+    for (hq, p), cubes in sel.items():
+        n = int(perm[p])
+        kv = hm[hq]
+        allowed = torch.tensor(np.isin(cube, list(cubes) + [p // g.S]))
+        s = (k[:, kv] @ qr[n, hq]) / math.sqrt(d)
+        o = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=0) @ v[:, kv]
+        loss = loss + o @ torch.tensor(dout[n, hq])
+    for (hq, m), cubes in selx.items():
+        kv = hm[hq]
+        allowed = torch.tensor(np.concatenate([np.isin(cube, cubes), np.arange(nt) <= m]))
+        s = (torch.cat([k[:, kv], kt[:, kv]]) @ qxt[m, hq]) / math.sqrt(d)
+        o = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=0) @ torch.cat([v[:, kv], vt[:, kv]])
+        loss = loss + o @ torch.tensor(dox[m, hq])
+    loss.backward()
+    np.testing.assert_allclose(res["dq_raster"], qr.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dq_extra"], qxt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dk_raster"], k.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dv_raster"], v.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dk_text"], kt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(res["dv_text"], vt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    # both KV heads receive gradient, and KV head 1 from two query heads
+    assert np.abs(res["dv_raster"][:, 0]).sum() > 0 and np.abs(res["dv_raster"][:, 1]).sum() > 0
