@@ -35,9 +35,9 @@ pytestmark = pytest.mark.gpu
 TOL_MAX, TOL_MEAN = 5e-2, 5e-3
 
 
-def _geom(wl):
+def _geom(wl, head_map=None):
     from adaptive_cube_sparse_amd import Geometry
-    return Geometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw, wl.n_q_heads, wl.n_kv_heads, wl.head_dim)
+    return Geometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, head_map)
 
 
 def _bf16_normal(rng, shape):
@@ -76,26 +76,27 @@ def _err(got, ref):
     return np.abs(got - ref) / np.maximum(rms, 1e-30)
 
 
-def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
+def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None, head_map=None):
     """Forward with log-sum-exp and backward on the device, graded against the
     float64 oracle over the device's selection.  video_rows: only these
     (hq, pos) rows are differentiated by the oracle (all rows by default);
     key_cubes: dK and dV are compared on the keys of these cubes only, which
     must be attended by listed rows alone (e.g. the last cubes when every row
-    of them is listed)."""
+    of them is listed); head_map: KV head of each query head (default
+    hq // (Hq / Hkv))."""
     from adaptive_cube_sparse_amd import AdasAttentionGrad
     p = wl.p if p is None else p
     n_extra = wl.n_text + wl.n_decode
     n_tk = wl.n_text if wl.text_kv else 0
     log(f"[bwd] {wl.name} grid {wl.T}x{wl.H}x{wl.W} cube ({wl.ct},{wl.ch},{wl.cw}) heads {wl.n_q_heads}/"
-        f"{wl.n_kv_heads} d {wl.head_dim} p {p} extra {n_extra} causal text keys {n_tk}")
+        f"{wl.n_kv_heads} d {wl.head_dim} p {p} extra {n_extra} causal text keys {n_tk} head_map {head_map}")
     data = workloads.generate(wl)
     g = O.Geometry.of(wl)
     dev = "cuda:0"
     rng = np.random.default_rng(seed)
     dout = _bf16_normal(rng, (g.N, wl.n_q_heads, wl.head_dim)) if wl.video_queries else None
     doutx = _bf16_normal(rng, (n_extra, wl.n_q_heads, wl.head_dim)) if n_extra else None
-    layer = AdasAttentionGrad(_geom(wl), p, has_video=wl.video_queries, n_extra=n_extra, device=dev,
+    layer = AdasAttentionGrad(_geom(wl, head_map), p, has_video=wl.video_queries, n_extra=n_extra, device=dev,
                               n_text_kv=n_tk)
     qx = to_dev(data["q_text"], dev) if n_extra else None
     kt = to_dev(data["k_text"], dev) if n_tk else None
@@ -111,7 +112,7 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
     v_cube, _ = O.partition(data["v"], g)
     ref = G.attention_grads(q_cube, k_cube, v_cube, g, sv, dout if dout is not None else np.zeros((g.N, wl.n_q_heads, wl.head_dim)),
                             data.get("q_text"), sx, doutx, k_text=data.get("k_text") if n_tk else None,
-                            v_text=data.get("v_text") if n_tk else None)
+                            v_text=data.get("v_text") if n_tk else None, head_map=head_map)
     # log-sum-exp
     lse = layer.lse.cpu().numpy()
     lerr = 0.0
@@ -130,7 +131,7 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None):
     worst = 0.0
     rows = [("v", k) for k in sv] + [("x", k) for k in sx]
     for kind, (hq, r) in rows:
-        kv = hq // (wl.n_q_heads // wl.n_kv_heads)
+        kv = head_map[hq] if head_map is not None else hq // (wl.n_q_heads // wl.n_kv_heads)
         if kind == "v":
             cubes = sorted(set(sv[(hq, r)]) | {r // g.S})
             n = int(perm[r])
@@ -205,6 +206,14 @@ def test_bwd_text_only_prefill_two_text_key_rounds():
     # no video rows; 70 text rows (the text kernels' rounds of 64 keys and
     # rows end in a partial round)
     _run_case(_small(name="bwd_text_only", video_queries=False, n_text=70, text_kv=True, seed=4108), p=0.5)
+
+
+def test_bwd_uneven_head_groups_with_text_keys():
+    # 5 query heads on 2 KV heads mapped [0, 0, 1, 1, 1] (groups of 2 and 3):
+    # union tiles and key-block row lists span groups of different sizes, and
+    # the text keys' dK / dV sum over a group's heads
+    _run_case(_small(name="bwd_head_map", n_q_heads=5, n_kv_heads=2, n_text=12, text_kv=True, seed=4109),
+              head_map=[0, 0, 1, 1, 1])
 
 
 def test_bwd_many_cubes_and_tiles():
