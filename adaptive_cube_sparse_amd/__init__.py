@@ -31,12 +31,13 @@ from ._lib import (  # noqa: F401
     adas_cube_mean_keys, adas_cube_partition, adas_cube_partition_keys, adas_select_topk, adas_select_topp,
     adas_sel_capacity,
     adas_sparse_attn_fwd, adas_version, adas_workspace_bytes, load, adas_sparse_attn_fwd_noalloc,
+    adas_decode_step, ADAS_WS_DECODE,
 )
 
 __all__ = [
     "Geometry", "AdasAttention", "AdasError", "adas_cube_partition", "adas_cube_mean_keys",
     "adas_cube_partition_keys",
-    "adas_select_topp", "adas_select_topk", "adas_sparse_attn_fwd", "adas_workspace_bytes",
+    "adas_select_topp", "adas_select_topk", "adas_sparse_attn_fwd", "adas_decode_step", "adas_workspace_bytes",
     "adas_sel_capacity",
     "adas_version", "load", "LIB_PATH",
     "FfnGeometry", "AdasFFN", "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
@@ -117,9 +118,18 @@ class AdasAttention:
         return self.out_raster, self.out_extra
 
     def decode_step(self, q_extra, stream=None):
-        """Selection plus attention for extra rows over an already built cache."""
-        self.select(q_extra, stream=stream)
-        self.attend(q_extra, None, None, stream)
+        """Selection plus attention for extra rows over an already built cache:
+        one adas_decode_step call (Top-p, no video rows, no text keys), else
+        the selection and attention calls in turn."""
+        if self.has_video or self.n_text_kv or self.topk is not None:
+            self.select(q_extra, stream=stream)
+            self.attend(q_extra, None, None, stream)
+            return self.out_extra
+        if getattr(self, "ws_decode", None) is None:
+            wsd = adas_workspace_bytes(self.geom, self.dtype, ADAS_WS_DECODE, False, self.n_extra)
+            self.ws_decode = torch.empty((max(wsd, 1),), device=self.kbar.device, dtype=torch.uint8)
+        adas_decode_step(self.geom, q_extra, self.kbar, self.k_cube, self.v_cube, self.p, self.sel_count,
+                         self.sel_idx, self.out_extra, self.ws_decode, stream)
         return self.out_extra
 
 

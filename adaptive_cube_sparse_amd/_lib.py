@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libadas.so")
 ADAS_OK, ADAS_ERR_NULL, ADAS_ERR_SHAPE, ADAS_ERR_VALUE, ADAS_ERR_DTYPE, \
     ADAS_ERR_WORKSPACE, ADAS_ERR_CAPACITY, ADAS_ERR_HIP = range(8)
 ADAS_BF16, ADAS_F32 = 0, 1
-ADAS_WS_SELECT, ADAS_WS_ATTN, ADAS_WS_BWD = 0, 1, 2
+ADAS_WS_SELECT, ADAS_WS_ATTN, ADAS_WS_BWD, ADAS_WS_DECODE = 0, 1, 2, 3
 ADAS_LAYOUT_TOKENS, ADAS_LAYOUT_VT = 0, 1
 ADAS_MAX_HEADS = 128
 ADAS_MAX_CUBES = 4096
@@ -34,7 +34,7 @@ EXPORTS = (
     "adas_ffn_select", "adas_ffn_fwd", "adas_ffn_workspace_bytes",
     "adas_cache_append", "adas_cache_sum_bytes", "adas_sparse_attn_fwd_lse", "adas_sparse_attn_bwd",
     "adas_probe_mfma", "adas_probe_hbm_read", "adas_probe_hbm_copy", "adas_sparse_attn_fwd_noalloc",
-    "adas_cube_partition_keys", "adas_probe_attn_mix",
+    "adas_cube_partition_keys", "adas_probe_attn_mix", "adas_decode_step",
 )
 
 
@@ -98,6 +98,7 @@ def load() -> ctypes.CDLL:
         "adas_probe_hbm_read": (i32, [vp, i64, vp, i32, vp]),
         "adas_probe_hbm_copy": (i32, [vp, vp, i64, i32, vp]),
         "adas_probe_attn_mix": (i32, [i32, i32, i32, vp, i64, vp, ctypes.POINTER(f64), vp]),
+        "adas_decode_step": (i32, [gp, i32, i32, vp, vp, vp, vp, f32, vp, vp, i64, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -302,6 +303,29 @@ def adas_sparse_attn_fwd_noalloc(geom: Geometry, q_cube, k_cube, v_cube, q_extra
                       out_raster, out_extra)
     st = load().adas_sparse_attn_fwd_noalloc(*args, _stream(stream))
     _check(st, "adas_sparse_attn_fwd_noalloc")
+
+
+def adas_decode_step(geom: Geometry, q_extra: torch.Tensor, kbar: torch.Tensor, k_cube: torch.Tensor,
+                     v_cube: torch.Tensor, p: float, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                     out_extra: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Selection and attention of n_extra query tokens over a built cache in
+    one call (q_extra, out_extra [n_extra][Hq][d]); see adas.h."""
+    n_extra = q_extra.shape[0]
+    Hq, Hkv, d = geom.n_q_heads, geom.n_kv_heads, geom.head_dim
+    _shape(q_extra, (n_extra, Hq, d), "q_extra")
+    _shape(out_extra, (n_extra, Hq, d), "out_extra")
+    _shape(k_cube, (Hkv, geom.NS, d), "k_cube")
+    _shape(v_cube, (Hkv, geom.NS // geom.S, d, geom.S), "v_cube")  # ADAS_LAYOUT_VT
+    _shape(sel_count, (Hq, n_extra), "sel_count")
+    dt = q_extra.dtype
+    g, keep = geom._c()
+    st = load().adas_decode_step(ctypes.byref(g), _dtype_code(q_extra), n_extra, _ptr(q_extra, dt, "q_extra"),
+                                 _ptr(kbar, torch.float32, "kbar"), _ptr(k_cube, dt, "k_cube"),
+                                 _ptr(v_cube, dt, "v_cube"), float(p), _ptr(sel_count, torch.int32, "sel_count"),
+                                 _ptr(sel_idx, torch.int32, "sel_idx"), sel_idx.numel(),
+                                 _ptr(out_extra, dt, "out_extra"), _ptr(ws, name="ws"),
+                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "adas_decode_step")
 
 
 def _attn_args(geom: Geometry, q_cube, k_cube, v_cube, q_extra, k_text, v_text, sel_count, sel_idx,

@@ -185,7 +185,7 @@ static adas_status select_common(const adas_geom* geom, adas_dtype dtype, const 
   const size_t ws_need = adas::select_workspace_bytes(g, dtype, n_extra, hg.gmax);
   if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need))
     return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_need);
-  adas::SelectArgs a;
+  adas::SelectArgs a{};
   a.g = g;
   a.zbuf = (float*)ws;
   a.hg = hg;
@@ -298,6 +298,68 @@ adas_status adas_sparse_attn_fwd_lse(const adas_geom* geom, adas_dtype dtype, co
                   sel_count, sel_idx, out_raster, out_extra, lse, ws, ws_bytes, stream);
 }
 
+// Workspace of adas_decode_step: the attention's part first, then the
+// selection's at a 256-byte aligned offset.
+static adas_status decode_plan(const adas_geom* geom, adas_dtype dtype, int32_t n_extra, adas::AttnArgs& a,
+                               size_t& attn_bytes, size_t& sel_off, size_t& total) {
+  if (n_extra < 1) return fail(ADAS_ERR_SHAPE, "n_extra must be >= 1 (got %d)", n_extra);
+  adas_status st = build_attn(geom, dtype, nullptr, n_extra, 0, a);
+  if (st != ADAS_OK) return st;
+  attn_bytes = adas::attention_workspace_bytes(a, dtype);
+  sel_off = (attn_bytes + 255) & ~(size_t)255;
+  total = sel_off + adas::select_workspace_bytes(a.g, dtype, n_extra, a.hg.gmax);
+  return ADAS_OK;
+}
+
+adas_status adas_decode_step(const adas_geom* geom, adas_dtype dtype, int32_t n_extra, const void* q_extra,
+                             const float* kbar, const void* k_cube, const void* v_cube, float p,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* out_extra,
+                             void* ws, size_t ws_bytes, void* stream) {
+  adas::AttnArgs a;
+  size_t attn_bytes = 0, sel_off = 0, need = 0;
+  adas_status st = decode_plan(geom, dtype, n_extra, a, attn_bytes, sel_off, need);
+  if (st != ADAS_OK) return st;
+  if (!(p > 0.0f && p <= 1.0f)) return fail(ADAS_ERR_VALUE, "p must be in (0, 1] (got %g)", (double)p);
+  if (q_extra == nullptr || kbar == nullptr || k_cube == nullptr || v_cube == nullptr || sel_count == nullptr ||
+      sel_idx == nullptr || out_extra == nullptr)
+    return fail(ADAS_ERR_NULL, "q_extra/kbar/k_cube/v_cube/sel_count/sel_idx/out_extra is NULL");
+  const int64_t cap = capacity_of(a.g, false, n_extra);
+  if (sel_cap < cap)
+    return fail(ADAS_ERR_CAPACITY, "sel_cap %lld < required %lld", (long long)sel_cap, (long long)cap);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(ADAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  a.k_cube = k_cube;
+  a.v_cube = v_cube;
+  a.q_extra = q_extra;
+  a.sel_count = sel_count;
+  a.sel_idx = sel_idx;
+  a.out_extra = out_extra;
+  adas::bind_attention_workspace(a, dtype, ws);
+  adas::SelectArgs s{};
+  s.g = a.g;
+  s.hg = a.hg;
+  s.q_extra = q_extra;
+  s.kbar = kbar;
+  s.zbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + sel_off);
+  s.n_extra = n_extra;
+  s.p = p;
+  s.sel_count = sel_count;
+  s.sel_idx = sel_idx;
+  s.capv = 0;
+  s.rows_per_head = n_extra;
+  s.has_video = 0;
+  // the split selection writes the extra rows' bitmaps the attention reads,
+  // so the attention skips its bitmap launch
+  if (dtype == ADAS_BF16 && a.extra_bits != nullptr && adas::use_split_select(a.g, n_extra, a.hg.gmax)) {
+    s.extra_bits = a.extra_bits;
+    s.bits_words = a.bits_words;
+    a.bits_ready = 1;
+  }
+  hipError_t e = adas::launch_select(s, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "adas_decode_step selection launch");
+  return hip_status(adas::launch_attention(a, dtype, (hipStream_t)stream), "adas_decode_step attention launch");
+}
+
 static adas_status build_bwd(const adas_geom* geom, adas_dtype dtype, bool has_video, int32_t n_extra,
                              adas::BwdArgs& b) {
   b = adas::BwdArgs{};
@@ -406,6 +468,12 @@ size_t adas_workspace_bytes(const adas_geom* geom, adas_dtype dtype, adas_ws_kin
     if (derive(geom, g, hg) != ADAS_OK || check_dtype(dtype) != ADAS_OK) return 0;
     if (n_extra < 0) return 0;
     return adas::select_workspace_bytes(g, dtype, n_extra, hg.gmax);
+  }
+  if (kind == ADAS_WS_DECODE) {
+    adas::AttnArgs a;
+    size_t attn_bytes = 0, sel_off = 0, total = 0;
+    if (has_video || decode_plan(geom, dtype, n_extra, a, attn_bytes, sel_off, total) != ADAS_OK) return 0;
+    return total;
   }
   if (kind == ADAS_WS_BWD) {
     adas::BwdArgs b;

@@ -272,7 +272,7 @@ void bind_attention_workspace(AttnArgs& a, adas_dtype dt, void* ws) {
 
 hipError_t launch_attention(const AttnArgs& a, adas_dtype dt, hipStream_t s) {
   if (dt == ADAS_BF16) {
-    if (a.n_extra > 0) {
+    if (a.n_extra > 0 && !a.bits_ready) {
       hipLaunchKernelGGL(k_extra_bitmap, dim3((unsigned)(a.g.Hq * a.n_extra)), dim3(256), 0, s, a);
       const hipError_t eb = hipGetLastError();
       if (eb != hipSuccess) return eb;

@@ -377,6 +377,10 @@ struct SelectArgs {
   int64_t capv;  // per-head video capacity (0 without video rows)
   int rows_per_head;  // Nv + n_extra
   int has_video;
+  // optional (split path, Top-p): also write each extra row's selection as a
+  // bitmap [Hq*n_extra][bits_words], bit j%32 of word j/32 for cube j
+  uint32_t* extra_bits;
+  int bits_words;
 };
 hipError_t launch_select(const SelectArgs& a, adas_dtype dt, hipStream_t s);
 size_t select_workspace_bytes(const KGeom& g, adas_dtype dt, int n_extra, int gmax);
@@ -399,6 +403,7 @@ struct AttnArgs {
   float* lse;            // optional [Hq][rows_per_head]: natural log-sum-exp of each row's scaled scores
   uint32_t* extra_bits;  // workspace: selection bitmap of extra rows [Hq*n_extra][bits_words]
   int bits_words;        // ceil(Nc / 32)
+  int bits_ready;        // the selection already wrote extra_bits (no bitmap launch)
   int n_extra;
   int n_text_kv;
   int64_t capv;

@@ -456,8 +456,14 @@ __global__ __launch_bounds__(64 * SW) void k_select_rows(SelectArgs a) {
   block_sum(zs, 0, Z, dummy);
   const int64_t off = extra_list_offset(a.capv, g.Hq, a.n_extra, g.Nc, hq, m);
   int32_t* out = a.sel_idx + off;
+  uint32_t* const bits = a.extra_bits != nullptr ? a.extra_bits + (size_t)row * a.bits_words : nullptr;
   if (a.p >= 1.0f) {
     for (int j = threadIdx.x; j < n; j += blockDim.x) out[j] = j;
+    if (bits != nullptr)
+      for (int w = threadIdx.x; w < a.bits_words; w += blockDim.x) {
+        const int left = n - 32 * w;  // >= 1: bits_words = ceil(n / 32)
+        bits[w] = left >= 32 ? 0xFFFFFFFFu : (1u << left) - 1u;
+      }
     if (threadIdx.x == 0) a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? g.N : 0) + m] = n;
     return;
   }
@@ -594,6 +600,12 @@ __global__ __launch_bounds__(64 * SW) void k_select_rows(SelectArgs a) {
     if (sel) out[base + lanes_below(bs)] = wave * C + kWave * i + lane;
     base += popc64(bs);
     eq_seen += popc64(beq);
+    // candidates wave*C + 64*i + lane are bits of words w0 (lanes 0..31) and
+    // w0 + 1 (lanes 32..63); every word below bits_words has one writer
+    if (bits != nullptr) {
+      const int w0 = (wave * C + kWave * i) >> 5;
+      if (lane < 2 && w0 + lane < a.bits_words) bits[w0 + lane] = (uint32_t)(bs >> (32 * lane));
+    }
   }
   if (threadIdx.x == 0) a.sel_count[(size_t)hq * a.rows_per_head + (a.has_video ? g.N : 0) + m] = total;
 }

@@ -86,7 +86,7 @@ typedef struct {
 } adas_geom;
 
 /* Which call a workspace is sized for. */
-typedef enum { ADAS_WS_SELECT = 0, ADAS_WS_ATTN = 1, ADAS_WS_BWD = 2 } adas_ws_kind;
+typedef enum { ADAS_WS_SELECT = 0, ADAS_WS_ATTN = 1, ADAS_WS_BWD = 2, ADAS_WS_DECODE = 3 } adas_ws_kind;
 
 /* Storage of a cube-layout tensor (see adas_cube_partition). */
 typedef enum { ADAS_LAYOUT_TOKENS = 0, ADAS_LAYOUT_VT = 1 } adas_layout;
@@ -246,6 +246,34 @@ adas_status adas_sparse_attn_fwd_lse(const adas_geom* geom, adas_dtype dtype, co
                                      const void* v_text, const int32_t* sel_count,
                                      const int32_t* sel_idx, void* out_raster, void* out_extra,
                                      float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * adas_decode_step -- one decode step over a built KV cache: the selection of
+ * adas_select_topp and the attention of adas_sparse_attn_fwd for n_extra
+ * query tokens with no video rows and no text keys (papernotes.org, key
+ * design 2; the AdaSpark listing, thelatestinai.com, Figure 2 caption: every
+ * token query selects its own cubes), in one call.  Results equal those of
+ * the two calls on the same inputs, bit for bit.  When the bf16 selection
+ * runs its split path (more than 1024 cubes, at most 64 query rows per KV
+ * head), it also writes each row's selection bitmap into ws, and the
+ * attention reads it instead of building it in a launch of its own.
+ *   n_extra  query tokens (>= 1)
+ *   q_extra  [n_extra][Hq][d], token-major
+ *   kbar     [Hkv][Nc][d] float32 mean keys of the cache
+ *   k_cube   [Hkv][N][d] ADAS_LAYOUT_TOKENS; v_cube [Hkv][Nc][d][S] ADAS_LAYOUT_VT
+ *   p        Top-p threshold in (0, 1]
+ *   sel_count [Hq][n_extra], sel_idx [sel_cap]: the selection, laid out as
+ *            adas_select_topp lays out extra rows (sel_cap >=
+ *            adas_sel_capacity(geom, 0, n_extra))
+ *   out_extra [n_extra][Hq][d]
+ *   ws, ws_bytes  adas_workspace_bytes(ADAS_WS_DECODE, has_video = 0, n_extra)
+ * Errors: NULL, SHAPE (n_extra < 1, Nc > ADAS_MAX_CUBES, ...), VALUE (p,
+ *         head_map), DTYPE, CAPACITY, WORKSPACE, HIP.
+ */
+adas_status adas_decode_step(const adas_geom* geom, adas_dtype dtype, int32_t n_extra, const void* q_extra,
+                             const float* kbar, const void* k_cube, const void* v_cube, float p,
+                             int32_t* sel_count, int32_t* sel_idx, int64_t sel_cap, void* out_extra,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * adas_sparse_attn_bwd -- gradients of the sparse attention for fine-tuning

@@ -135,6 +135,46 @@ def test_select_rejects_invalid_arguments_on_host():
     assert _select(lib, g2) == L.ADAS_ERR_VALUE
 
 
+def test_decode_step_workspace_and_host_validation():
+    import adaptive_cube_sparse_amd._lib as L
+    lib = L.load()
+    big = _geom(T=64, H=64, W=64)  # 4096 cubes: the split selection, the decode kernel
+    n = 1
+    attn = lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_ATTN, 0, n)
+    sel = lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_SELECT, 0, n)
+    dec = lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_DECODE, 0, n)
+    assert attn > 0 and sel == 6 * n * 4096 * 4
+    # the attention's part of a decode plan (no text keys: the decode kernel, about one workgroup per CU,
+    # 256 / Hkv = 128 chunks of 32 cubes): the extra-row bitmap (128 words per row) and one partial row
+    # (max, sum, d outputs) per (KV head, 32-row slot, chunk); then the selection's logits
+    bitmap = 6 * n * 128 * 4
+    partials = 2 * 32 * 128 * (128 + 2) * 4
+    attn_decode = ((bitmap + 255) // 256) * 256 + partials
+    assert dec == ((attn_decode + 255) // 256) * 256 + sel
+    assert dec < attn + sel   # ADAS_WS_ATTN also covers the text-key plan (union tiles)
+    assert lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_DECODE, 1, n) == 0  # no video rows
+    assert lib.adas_workspace_bytes(ctypes.byref(big), L.ADAS_BF16, L.ADAS_WS_DECODE, 0, 0) == 0
+
+    def step(g, **kw):
+        a = dict(dtype=L.ADAS_BF16, n=n, q=FAKE, kbar=FAKE, k=FAKE, v=FAKE, p=0.7, cnt=FAKE, idx=FAKE,
+                 cap=1 << 40, out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.adas_decode_step(ctypes.byref(g) if g is not None else None, a["dtype"], a["n"], a["q"],
+                                    a["kbar"], a["k"], a["v"], a["p"], a["cnt"], a["idx"], a["cap"], a["out"],
+                                    a["ws"], a["ws_bytes"], None)
+    assert step(None) == L.ADAS_ERR_NULL
+    assert step(big, n=0) == L.ADAS_ERR_SHAPE
+    for p in (0.0, 1.5, float("nan")):
+        assert step(big, p=p) == L.ADAS_ERR_VALUE
+    for k in ("q", "kbar", "k", "v", "cnt", "idx", "out"):
+        assert step(big, **{k: None}) == L.ADAS_ERR_NULL
+    assert step(big, dtype=9) == L.ADAS_ERR_DTYPE
+    assert step(big, cap=6 * 4096 - 1) == L.ADAS_ERR_CAPACITY
+    assert step(big, ws_bytes=dec - 1) == L.ADAS_ERR_WORKSPACE
+    assert step(big, ws=None, ws_bytes=0) == L.ADAS_ERR_WORKSPACE
+    assert step(_geom(ct=3)) == L.ADAS_ERR_SHAPE
+
+
 def test_topk_rejects_invalid_arguments_on_host():
     import adaptive_cube_sparse_amd._lib as L
     lib = L.load()

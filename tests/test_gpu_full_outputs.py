@@ -89,8 +89,12 @@ def _stratified_cubes(nc, seed, per_decile=2):
     return sorted(cubes)
 
 
-@pytest.mark.parametrize("name", ["qwen7b_p05", "qwen7b_p07", "qwen7b_p09", "hour"])
+# the hour-scale layer's sample runs as two tests (alternate cubes of the
+# sample; the text rows with the second), each well under the runner's
+# silence limit
+@pytest.mark.parametrize("name", ["qwen7b_p05", "qwen7b_p07", "qwen7b_p09", "hour:0", "hour:1"])
 def test_stratified_whole_cube_outputs(name):
+    name, part = (name.split(":") + [None])[:2]
     wl = workloads.get(name)
     data = workloads.generate(wl)
     layer = run_device(wl, data)
@@ -98,8 +102,11 @@ def test_stratified_whole_cube_outputs(name):
     check_layout(ref, layer)
     g, S, Hq = ref.g, ref.g.S, wl.n_q_heads
     cubes = _stratified_cubes(g.n_cubes, seed=7000 + len(name))
+    with_text = part in (None, "1")
+    if part is not None:
+        cubes = cubes[int(part)::2]
     log(f"case {name}: every row of query cubes {cubes}, all heads"
-        + (f", and all {wl.n_text} text rows" if wl.n_text else ""))
+        + (f", and all {wl.n_text} text rows" if wl.n_text and with_text else ""))
     cnt = layer.sel_count.cpu().numpy()
     out_r = bits(layer.out_raster)
     tasks, n_rows = [], 0
@@ -114,7 +121,7 @@ def test_stratified_whole_cube_outputs(name):
             rows = [(int(p), seg[r * c:r * c + k[r]]) for r, p in enumerate(pos)]
             tasks.append(("v", hq, rows, out_r[ref.perm[pos], hq]))
             n_rows += S
-    if ref.n_extra:
+    if ref.n_extra and with_text:
         out_x = bits(layer.out_extra)
         for hq in range(Hq):
             base = ref.extra_off(hq, 0)

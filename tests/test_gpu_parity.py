@@ -234,3 +234,64 @@ def test_decode_single_step():
     """One decode step (1 query token x 28 heads) over the full decode cache."""
     wl = workloads.get("decode").replace(n_decode=1, name="decode_step")
     _case(wl)
+
+
+# --- one-call decode step (selection + attention) --------------------------------------
+DECODE_STEP_CASES = {
+    # 4096 cubes, one query x 28 heads: split selection writes the bitmaps the decode kernel reads
+    "cache_4096_one_query": (workloads.get("decode").replace(n_decode=1), None, None),
+    # 2048 cubes, 3 queries, uneven head groups: the decode kernel with 9 rows per KV head
+    "cache_2048_head_map": (workloads.Workload(name="ds_2048", T=512, H=16, W=16, ct=4, ch=4, cw=4,
+                                               n_q_heads=5, n_kv_heads=2, head_dim=128, dtype="bf16",
+                                               p=0.6, seed=71, video_queries=False, n_decode=3),
+                            [0, 0, 1, 1, 1], None),
+    # p = 1: every cube, the bitmaps written by the all-selected branch
+    "cache_2048_p1": (workloads.Workload(name="ds_p1", T=512, H=16, W=16, ct=4, ch=4, cw=4, n_q_heads=4,
+                                         n_kv_heads=2, head_dim=64, dtype="bf16", p=1.0, seed=72,
+                                         video_queries=False, n_decode=2), None, None),
+    # 56 rows per KV head: split selection, but union tiles read the bitmaps
+    "cache_2048_union_tiles": (workloads.Workload(name="ds_union", T=512, H=16, W=16, ct=4, ch=4, cw=4,
+                                                  n_q_heads=7, n_kv_heads=1, head_dim=128, dtype="bf16",
+                                                  p=0.7, seed=73, video_queries=False, n_decode=8),
+                               None, None),
+    # 256 cubes: the band selection, the attention builds its own bitmaps
+    "cache_256_band_selection": (workloads.Workload(name="ds_band", T=64, H=16, W=16, ct=4, ch=4, cw=4,
+                                                    n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16",
+                                                    p=0.7, seed=74, video_queries=False, n_decode=2),
+                                 None, None),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DECODE_STEP_CASES))
+def test_decode_step_call_equals_select_then_attend(case):
+    from adaptive_cube_sparse_amd import AdasAttention
+    from tests.gpu_harness import geometry, to_dev
+    wl, head_map, _ = DECODE_STEP_CASES[case]
+    log(f"case {case}: adas_decode_step against adas_select_topp + adas_sparse_attn_fwd "
+        f"({wl.n_q_heads}/{wl.n_kv_heads} heads, {wl.T}x{wl.H}x{wl.W}, {wl.n_decode} queries, p {wl.p})")
+    data = workloads.generate(wl)
+    dev = torch.device("cuda:0")
+    layer = AdasAttention(geometry(wl, head_map), torch.bfloat16, wl.p, has_video=False,
+                          n_extra=wl.n_decode, device=dev)
+    layer.build_kv(to_dev(data["k"], dev), to_dev(data["v"], dev))
+    q = to_dev(data["q_text"], dev)
+    layer.select(q)
+    layer.attend(q)
+    torch.cuda.synchronize()
+    want = (layer.sel_count.clone(), layer.sel_idx.clone(), layer.out_extra.clone())
+    layer.sel_idx.fill_(-5)
+    layer.out_extra.zero_()
+    layer.decode_step(q)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.sel_count, want[0])
+    cnt = want[0].cpu().numpy()
+    got_idx, want_idx = layer.sel_idx.cpu().numpy(), want[1].cpu().numpy()
+    Nc = wl.T * wl.H * wl.W // (wl.ct * wl.ch * wl.cw)
+    for hq in range(wl.n_q_heads):
+        for m in range(wl.n_decode):
+            o = (hq * wl.n_decode + m) * Nc
+            assert np.array_equal(got_idx[o:o + cnt[hq, m]], want_idx[o:o + cnt[hq, m]]), (hq, m)
+    assert torch.equal(layer.out_extra.view(torch.int16), want[2].view(torch.int16))
+    # and the rows against the oracle
+    ref = Reference(wl, data, head_map)
+    check_rows(ref, layer, all_rows(ref), wl.p)
