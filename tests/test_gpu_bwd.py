@@ -48,16 +48,17 @@ def _lists(layer, wl, g, video_rows=None):
     """Device selection of every row (or of the video rows listed):
     ({(hq, pos): cubes}, {(hq, m): cubes})."""
     cnt = layer.sel_count.cpu().numpy()
-    idx = layer.sel_idx.cpu().numpy()
     capv = g.S * g.n_cubes * (g.n_cubes - 1) // 2 if wl.video_queries else 0
     n_extra = wl.n_text + wl.n_decode
     sv, sx = {}, {}
     if video_rows is not None:
+        # only the listed rows' entries leave the device
         for hq, p in video_rows:
             c, r = divmod(p, g.S)
             o = hq * capv + g.S * c * (c - 1) // 2 + r * c
-            sv[(hq, p)] = idx[o:o + cnt[hq, p]].tolist()
+            sv[(hq, p)] = layer.sel_idx[o:o + int(cnt[hq, p])].cpu().numpy().tolist()
         return sv, sx
+    idx = layer.sel_idx.cpu().numpy()
     for hq in range(wl.n_q_heads):
         if wl.video_queries:
             for p in range(g.N):
@@ -76,14 +77,17 @@ def _err(got, ref):
     return np.abs(got - ref) / np.maximum(rms, 1e-30)
 
 
-def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None, head_map=None):
+def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None, head_map=None, key_heads=None,
+              dq_rows=None):
     """Forward with log-sum-exp and backward on the device, graded against the
     float64 oracle over the device's selection.  video_rows: only these
     (hq, pos) rows are differentiated by the oracle (all rows by default);
     key_cubes: dK and dV are compared on the keys of these cubes only, which
     must be attended by listed rows alone (e.g. the last cubes when every row
-    of them is listed); head_map: KV head of each query head (default
-    hq // (Hq / Hkv))."""
+    of them is listed); key_heads: KV heads whose dK and dV are compared
+    (all by default); dq_rows: video rows (hq, pos) whose dq is held to its
+    bound (all differentiated rows by default); head_map: KV head of each
+    query head (default hq // (Hq / Hkv))."""
     from adaptive_cube_sparse_amd import AdasAttentionGrad
     p = wl.p if p is None else p
     n_extra = wl.n_text + wl.n_decode
@@ -129,7 +133,7 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None, head_map=None
     outx_dev = O.to_f64(bits(layer.fwd.out_extra)) if n_extra else None
     perm = O.partition(data["k"], g)[1]
     worst = 0.0
-    rows = [("v", k) for k in sv] + [("x", k) for k in sx]
+    rows = [("v", k) for k in sv if dq_rows is None or k in dq_rows] + [("x", k) for k in sx]
     for kind, (hq, r) in rows:
         kv = head_map[hq] if head_map is not None else hq // (wl.n_q_heads // wl.n_kv_heads)
         if kind == "v":
@@ -158,8 +162,9 @@ def _run_case(wl, p=None, seed=0, video_rows=None, key_cubes=None, head_map=None
     keys = slice(None)
     if key_cubes is not None:
         keys = np.sort(np.concatenate([perm[j * g.S:(j + 1) * g.S] for j in key_cubes]))
-    errs["dk"] = _err(dk.cpu().numpy()[keys], ref["dk_raster"][keys])
-    errs["dv"] = _err(dv.cpu().numpy()[keys], ref["dv_raster"][keys])
+    kh = slice(None) if key_heads is None else list(key_heads)
+    errs["dk"] = _err(dk.cpu().numpy()[keys][:, kh], ref["dk_raster"][keys][:, kh])
+    errs["dv"] = _err(dv.cpu().numpy()[keys][:, kh], ref["dv_raster"][keys][:, kh])
     if n_tk:
         errs["dk_text"] = _err(layer.dk_text.cpu().numpy(), ref["dk_text"])
         errs["dv_text"] = _err(layer.dv_text.cpu().numpy(), ref["dv_text"])
@@ -220,6 +225,26 @@ def test_bwd_many_cubes_and_tiles():
     # 64 cubes, 7 query heads per KV head: tiles of 256 rows span head slots,
     # early cubes are attended by hundreds of rows
     _run_case(_small(name="bwd_mid", T=16, H=16, W=16, n_q_heads=7, n_kv_heads=1, seed=4105), p=0.7)
+
+
+def test_bwd_qwen7b_full_size_sampled():
+    # the 7B-shaped layer bench.py --backward times (28/4 heads, 1024 cubes of
+    # 64, p = 0.7): every row of the last cube for the 7 query heads of KV
+    # head 0 (the last cube is attended by its own rows only, so dK and dV of
+    # its keys on KV head 0 are then complete sums) plus 2 rows per head in
+    # cubes spread over the layer
+    wl = workloads.get("qwen7b_p07")
+    g = O.Geometry.of(wl)
+    Nc, S = g.n_cubes, g.S
+    rng = np.random.default_rng(4110)
+    rows = {(hq, p) for hq in range(7) for p in range((Nc - 1) * S, Nc * S)}
+    for c in (0, 1, Nc // 4, Nc // 2, 3 * Nc // 4, Nc - 3):
+        for hq in range(wl.n_q_heads):
+            for r in rng.choice(S, size=2, replace=False):
+                rows.add((hq, c * S + int(r)))
+    spread = {(hq, p) for hq, p in rows if p < (Nc - 1) * S}
+    dq_rows = spread | {(hq, p) for hq, p in rows if p >= (Nc - 1) * S and p % 8 == hq}
+    _run_case(wl, video_rows=sorted(rows), key_cubes=[Nc - 1], key_heads=[0], dq_rows=dq_rows)
 
 
 def test_bwd_qwen3b_full_size_sampled():
