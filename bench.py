@@ -485,6 +485,7 @@ def cpu_baseline(wl, data, budget_s: float, topk: int = 0, sample_out=None):
             "sample": f"{rows} random rows of {wl.name} (selection softmax, Top-p and attention "
                       f"per row, float64 NumPy, 1 BLAS thread) in {t_rows:.1f} s; whole-input "
                       f"partition + mean keys took {t_layout:.1f} s and are not in the rate",
+            "rows_per_s": rows / t_rows, "layout_s": t_layout,
             "host_threads_available": len(os.sched_getaffinity(0))}
 
 
@@ -927,6 +928,9 @@ def main():
                         check["grades"][key] += part["grades"][key]
         else:
             check = grade_sample(layer, wl, sample, args.topk)
+        # the whole step's work at the sampled rate (rows weighted by their work:
+        # the step's attention FLOPs over the oracle's FLOP rate), plus its layout
+        cpu["full_step_s_extrapolated"] = flops_step / (cpu["value"] * 1e12) + cpu["layout_s"]
     dens = sel_stats.get("video_mean_selected_fraction", sel_stats["mean_selected_fraction"])
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
