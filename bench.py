@@ -301,6 +301,42 @@ def decode_step_ms(layer, qe_steps, used, flush, flush_sink, stream, graph: bool
     return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
 
 
+def stream_append_stage(wl, k, v, layer) -> dict:
+    """The same video cache built by the streaming path (StreamingCache.append,
+    one temporal block of ct frames per call, mean keys formed as each block
+    completes): mean event-timed duration per block, its bytes (K and V read
+    and written, the block's mean keys written) and whether the streamed cache
+    and mean keys equal the one-pass build bit for bit."""
+    import torch
+    from adaptive_cube_sparse_amd import StreamingCache
+    g = layer.geom
+    sc = StreamingCache(g, wl.p, device=k.device)
+    fr = g.H * g.W
+    pairs = []
+    for f0 in range(0, g.T, g.ct):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sc.append(k[f0 * fr:(f0 + g.ct) * fr], v[f0 * fr:(f0 + g.ct) * fr])
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in pairs[1:]]))  # the first call also warms up
+    elem = 2  # bf16
+    block = g.ct * fr * g.n_kv_heads * g.head_dim * elem * 2   # K and V of one block
+    kbar_bytes = (g.H // g.ch) * (g.W // g.cw) * g.n_kv_heads * g.head_dim * 4
+    nbytes = 2 * block + kbar_bytes
+    same = (torch.equal(sc.k_cache.view(torch.int16), layer.k_cube.view(torch.int16))
+            and torch.equal(sc.v_cache.view(torch.int16), layer.v_cube.view(torch.int16))
+            and torch.equal(sc.kbar, layer.kbar))
+    del sc
+    torch.cuda.empty_cache()
+    return {"ms_per_block": ms, "frames_per_block": g.ct, "blocks": len(pairs), "bytes_per_block": nbytes,
+            "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "matches_one_pass": bool(same),
+            "note": "adas_cache_append of one temporal block per call over the whole video, event-timed"}
+
+
 def peak_probes() -> dict:
     """Measured ceilings: an MFMA-only register loop (dense bf16), the same
     MFMAs with the union attention's side work per MFMA (LDS operand read,
@@ -892,6 +928,7 @@ def main():
                 "ms": sep_ms, "GB/s": sep_gbs, "frac": sep_gbs / PEAK_HBM_GBS,
                 "note": "adas_select_topp then adas_sparse_attn_fwd (its own bitmap launch), the timed loop's "
                         "select + attention events"}
+            stages["stream_append"] = stream_append_stage(wl, k, v, layer)
             g_ms = decode_step_ms(layer, qe_steps, used_queries, flush, flush_sink, stream, graph=True)
             g_gbs = alg_bytes / (g_ms * 1e-3) / 1e9
             stages["decode_step_graph"] = {

@@ -154,20 +154,14 @@ def test_ffn_several_column_tiles_and_k_stages():
     _case(wl)
 
 
-def test_ffn3b_full_size_sampled():
-    wl = workloads.get_ffn("ffn3b")
-    g = _og(wl)
-    rng = np.random.default_rng(0)
-    cubes = sorted({0, g.n_cubes - 1, *rng.integers(0, g.n_cubes, 4).tolist()})
-    _case(wl, cubes=cubes)
+def test_ffn3b_full_size_every_token():
+    # the 3B-shaped layer bench.py times: every token of all 256 cubes
+    _case(workloads.get_ffn("ffn3b"))
 
 
-def test_ffn7b_full_size_sampled():
-    wl = workloads.get_ffn("ffn7b")
-    g = _og(wl)
-    rng = np.random.default_rng(1)
-    cubes = sorted({0, g.n_cubes - 1, *rng.integers(0, g.n_cubes, 2).tolist()})
-    _case(wl, cubes=cubes)
+def test_ffn7b_full_size_every_token():
+    # the 7B-shaped layer bench.py times: every token of every cube
+    _case(workloads.get_ffn("ffn7b"))
 
 
 def test_ffn_deterministic():
