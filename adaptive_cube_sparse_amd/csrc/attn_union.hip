@@ -505,15 +505,9 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
   using U1 = std::integral_constant<int, 1>;
   using U2 = std::integral_constant<int, 2>;
   using U3 = std::integral_constant<int, 3>;
-  // one full block
+  // preC: whether the previous step already read the first operands
   using PF = std::false_type;
   using PT = std::true_type;
-  auto block1 = [&](const uint16_t* kb, const uint16_t* vb, bool sel) __attribute__((always_inline)) {
-    run_step(U0{}, UN{}, UN{}, kb, vb, sel, PF{}, U1{}, UN{}, kb, vb);
-    run_step(U1{}, UN{}, U0{}, kb, vb, sel, PT{}, UN{}, U0{}, kb, vb);
-    run_step(UN{}, U0{}, U1{}, kb, vb, sel, PT{}, UN{}, U1{}, kb, vb);
-    run_step(UN{}, U1{}, UN{}, kb, vb, sel, PT{}, UN{}, UN{}, kb, vb);
-  };
   // two full blocks
   auto block2 = [&](const uint16_t* kb0, const uint16_t* vb0, bool sel0, const uint16_t* kb1,
                     const uint16_t* vb1, bool sel1) __attribute__((always_inline)) {
@@ -588,7 +582,6 @@ __global__ __launch_bounds__(UNT, 1) void k_attn_union(AttnArgs a, USched sc) {
       dlds[m] = q * 1024;
     }
   }
-  typedef __attribute__((address_space(3))) void lds_void;
   // issue this wave's loads of the block whose K rows start at kb and whose
   // V^T rows start at vb (bytes), into buffer buf
   // Buffer loads into LDS (buffer_load_lds16), one descriptor per KV head's K
