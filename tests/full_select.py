@@ -1,4 +1,4 @@
-"""Whole-layer check of the device's Top-p lists against the oracle.
+"""Whole-layer check of the device's Top-p (or Top-K) lists against the oracle.
 
 Every row's set is compared, not a sample: the oracle computes each row's
 Top-p set (papernotes.org, AdaSpark, key design 2: S_i = Top-p(P_i, p)) and
@@ -51,9 +51,21 @@ def _rows_signature(P: np.ndarray, p: float, tag: np.ndarray):
     return k, sig.astype(np.int64), _near_flags(P, p, k)
 
 
-def video_head(q_head: np.ndarray, kbar_g: np.ndarray, S: int, p: float):
+def _rows_signature_topk(P: np.ndarray, k: int, tag: np.ndarray):
+    """Top-K counterpart of _rows_signature: each row's set from the oracle's
+    ``top_k``; no near-threshold notion (near is all False)."""
+    rows, n = P.shape
+    mask = np.zeros((rows, n), bool)
+    for r in range(rows):
+        mask[r, O.top_k(P[r], k)] = True
+    sig = (mask * tag[None, :n]).sum(axis=1) if n else np.zeros(rows, np.int64)
+    return mask.sum(axis=1).astype(np.int32), sig.astype(np.int64), np.zeros(rows, bool)
+
+
+def video_head(q_head: np.ndarray, kbar_g: np.ndarray, S: int, p: float, k: int | None = None):
     """One query head's video rows, cube by cube: q_head [N][d] (cube
     layout, bf16 bits or float32), kbar_g [Nc][d] float64 (exact means).
+    Top-K sets instead of Top-p when k is given.
     Returns (counts [N] int32, signatures [N] int64, near [N] bool)."""
     N, d = q_head.shape
     nc = N // S
@@ -64,18 +76,18 @@ def video_head(q_head: np.ndarray, kbar_g: np.ndarray, S: int, p: float):
     q64 = O.to_f64(q_head)
     for c in range(1, nc):
         P = O.selection_probabilities(q64[c * S:(c + 1) * S], kbar_g[:c])
-        k, s, nf = _rows_signature(P, p, tag)
-        counts[c * S:(c + 1) * S] = k
+        cnt, s, nf = _rows_signature(P, p, tag) if k is None else _rows_signature_topk(P, k, tag)
+        counts[c * S:(c + 1) * S] = cnt
         sig[c * S:(c + 1) * S] = s
         near[c * S:(c + 1) * S] = nf
     return counts, sig, near
 
 
-def extra_head(q_rows: np.ndarray, kbar_g: np.ndarray, p: float):
+def extra_head(q_rows: np.ndarray, kbar_g: np.ndarray, p: float, k: int | None = None):
     """Extra (text / decode) rows of one head over every cube: q_rows [m][d]."""
     tag = tags(kbar_g.shape[0])
     P = O.selection_probabilities(O.to_f64(q_rows), kbar_g)
-    return _rows_signature(P, p, tag)
+    return _rows_signature(P, p, tag) if k is None else _rows_signature_topk(P, k, tag)
 
 
 def _video_task(args):
@@ -85,9 +97,10 @@ def _video_task(args):
         return video_head(*args)
 
 
-def oracle_signatures(ref, p: float, workers: int | None = None):
+def oracle_signatures(ref, p: float, workers: int | None = None, k: int | None = None):
     """(counts, signatures, near) of every row, shaped [Hq][rows_per_head],
-    video rows first.  Per-head work runs in a pool of spawned processes."""
+    video rows first (Top-K sets when k is given).  Per-head work runs in a
+    pool of spawned processes."""
     wl, g = ref.wl, ref.g
     Hq = wl.n_q_heads
     R = ref.rows_per_head
@@ -96,7 +109,7 @@ def oracle_signatures(ref, p: float, workers: int | None = None):
     near = np.zeros((Hq, R), bool)
     nv = g.N if wl.video_queries else 0
     if wl.video_queries:
-        tasks = [(ref.q_cube[hq], ref.kbar[ref.kv(hq)], g.S, p) for hq in range(Hq)]
+        tasks = [(ref.q_cube[hq], ref.kbar[ref.kv(hq)], g.S, p, k) for hq in range(Hq)]
         if workers is None:
             workers = min(16, len(os.sched_getaffinity(0)), Hq)
         if workers > 1:
@@ -108,7 +121,7 @@ def oracle_signatures(ref, p: float, workers: int | None = None):
             counts[hq, :nv], sig[hq, :nv], near[hq, :nv] = c, s, nf
     if ref.n_extra:
         for hq in range(Hq):
-            c, s, nf = extra_head(ref.data["q_text"][:, hq], ref.kbar[ref.kv(hq)], p)
+            c, s, nf = extra_head(ref.data["q_text"][:, hq], ref.kbar[ref.kv(hq)], p, k)
             counts[hq, nv:], sig[hq, nv:], near[hq, nv:] = c, s, nf
     return counts, sig, near
 

@@ -1,5 +1,6 @@
 """Full-size layers, and a layer at the cube limit: every row's Top-p list
-against the oracle (not a sample).
+against the oracle (not a sample); and every row's Top-K list of the 3B, 7B
+and hour-scale layers.
 
 The oracle's whole-layer selection runs in worker processes (one task per
 query head); the device lists are reduced to per-row signatures on the GPU
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 
 import workloads
-from oracle.compare import grade_row
+from oracle.compare import grade_row, grade_row_topk
 from tests.full_select import oracle_signatures, tags
 from tests.gpu_harness import ALARM_FRAC, Reference, check_layout, check_rows, fetch_lists, log, \
     run_device, sampled_rows, selection_probs
@@ -94,3 +95,35 @@ def test_full_selection_lists(name):
     if name == "max_cubes":
         # outputs of this layer on a stratified sample of rows
         check_rows(ref, layer, sampled_rows(ref, cubes_per_decile=2, tokens_per_cube=4), wl.p)
+
+
+# Top-K over whole layers (the fixed-budget rule of the AdaSpark listing,
+# thelatestinai.com, Table 4): k is about the Top-p rule's mean cubes per row
+# on each layer, so rows of early cubes keep every candidate and later rows
+# cut inside the candidate set.
+@pytest.mark.parametrize("name,k", [("qwen3b", 23), ("qwen7b_p07", 161), ("hour", 314)])
+def test_full_topk_lists(name, k):
+    wl = workloads.get(name)
+    log(f"case {name}: full Top-K check, k {k}, {wl.n_q_heads} heads")
+    data = workloads.generate(wl)
+    layer = run_device(wl, data, k=k)
+    ref = Reference(wl, data)
+    check_layout(ref, layer)
+    t0 = time.time()
+    dc, ds = device_signatures(layer, ref)
+    oc, osig, _ = oracle_signatures(ref, wl.p, k=k)
+    log(f"  oracle Top-K of {oc.size} rows in {time.time() - t0:.1f} s")
+    bad = np.argwhere((dc != oc) | (ds != osig))
+    nv = ref.g.N if wl.video_queries else 0
+    rows = [("v", int(h), int(r)) if r < nv else ("x", int(h), int(r - nv)) for h, r in bad]
+    grades = {"exact": int(oc.size - len(rows)), "near_tie": 0, "fail": 0}
+    fails = []
+    for (kind, hq, i), S in zip(rows, fetch_lists(ref, layer, rows)):
+        P, z, bnd = selection_probs(ref, kind, hq, i)
+        gr = grade_row_topk(P, k, S, z, bnd)
+        grades[gr] += 1
+        if gr == "fail" and len(fails) < 5:
+            fails.append((kind, hq, i, S[:12].tolist()))
+    log(f"  grades over all {oc.size} rows: {grades}")
+    assert grades["fail"] == 0, f"Top-K failures: {fails}"
+    assert grades["near_tie"] <= max(2, ALARM_FRAC * oc.size)
