@@ -1,6 +1,6 @@
 """Full-size layers, and a layer at the cube limit: every row's Top-p list
-against the oracle (not a sample); and every row's Top-K list of the 3B, 7B
-and hour-scale layers.
+against the oracle (not a sample); and every row's Top-K list of the 3B, 7B,
+hour-scale and decode layers.
 
 The oracle's whole-layer selection runs in worker processes (one task per
 query head); the device lists are reduced to per-row signatures on the GPU
@@ -101,7 +101,7 @@ def test_full_selection_lists(name):
 # thelatestinai.com, Table 4): k is about the Top-p rule's mean cubes per row
 # on each layer, so rows of early cubes keep every candidate and later rows
 # cut inside the candidate set.
-@pytest.mark.parametrize("name,k", [("qwen3b", 23), ("qwen7b_p07", 161), ("hour", 314)])
+@pytest.mark.parametrize("name,k", [("qwen3b", 23), ("qwen7b_p07", 161), ("hour", 314), ("decode", 1305)])
 def test_full_topk_lists(name, k):
     wl = workloads.get(name)
     log(f"case {name}: full Top-K check, k {k}, {wl.n_q_heads} heads")
