@@ -71,6 +71,28 @@ def test_stream_append_matches_one_pass(chunks):
     log(f"  {f} frames appended; cache and mean keys match the one-pass layout after every chunk")
 
 
+def test_stream_full_decode_cache():
+    # the decode workload's whole cache (1024 frames of 16x16, 4 KV heads,
+    # 4096 cubes) appended in uneven chunks that cross block boundaries:
+    # checked mid-block after the second chunk and whole at the end
+    from adaptive_cube_sparse_amd import Geometry, StreamingCache
+    wl = workloads.get("decode")
+    log(f"[stream] full cache {wl.T}x{wl.H}x{wl.W}, {wl.n_kv_heads} KV heads, chunks 3, 258, 763 frames")
+    data = workloads.generate(wl)
+    dev = "cuda:0"
+    geom = Geometry(wl.T, wl.H, wl.W, wl.ct, wl.ch, wl.cw, wl.n_q_heads, wl.n_kv_heads, wl.head_dim)
+    cache = StreamingCache(geom, wl.p, device=dev)
+    hw = wl.H * wl.W
+    f = 0
+    for n in (3, 258, 763):
+        cache.append(to_dev(data["k"][f * hw:(f + n) * hw], dev), to_dev(data["v"][f * hw:(f + n) * hw], dev))
+        f += n
+        torch.cuda.synchronize()
+        if f in (261, wl.T):
+            _check_prefix(cache, data, wl, f)
+            log(f"  {f} frames: cache and mean keys equal the one-pass layout")
+
+
 def test_stream_decode_over_completed_cubes():
     from adaptive_cube_sparse_amd import AdasAttention, Geometry, StreamingCache
     wl = _wl()
